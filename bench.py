@@ -1,0 +1,432 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused all-reduce epilogue + residual + RMSNorm (+ FP4) on
+one MI355X.
+
+A step is one fused call (all of: rank-ordered sum of N bf16 partials,
+residual add, residual_out store, RMSNorm, bf16 store) over one batch of
+synthetic input resident in HBM. The timed workload is the prefill bandwidth
+shape: N = 8 partials, t = 4096 tokens, d = 8192 (64 MiB per partial), with
+0.1% outlier rows in the residual. Buffer sets rotate so that no call can be
+served from the 256 MB Infinity Cache.
+
+`value` is GB/s counted as ((N + 2) reads + 2 writes) x t x d x 2 bytes, the
+counting the workload definition asks for. `roofline.achieved` uses the
+algorithmic bytes instead (N partials + residual + gamma read, residual_out +
+y written). The decode shapes (single token; Llama-3-8B and Llama-3.1-70B
+decode steps as 64- and 160-call hipGraph chains, plain and LL-packed) and
+the FP4 shapes are reported under "extras" as µs per call against the
+measured floor of an empty kernel with the same launch in the same graph.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published peak
+INFINITY_CACHE_BYTES = 256 << 20
+METRIC = "fused kernel HBM GB/s (% of peak) at prefill; µs/call p50 at decode shapes"
+KERNEL_SRC = os.path.join(ROOT, "reduce_residual_rmsnorm_amd", "csrc", "arfuse.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg: str) -> None:
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ byte accounting
+
+def plane_bytes(t: int, d: int) -> int:
+    """One bf16 [t][d] tensor: t x d x 2 bytes (the all-reduce message size of
+    tensor parallelism, independent of the rank count)."""
+    return t * d * 2
+
+
+def algorithmic_bytes(n: int, t: int, d: int, ll: bool = False, out: bool = True,
+                      fp4: bool = False):
+    """(read, write) bytes one fused call must move: N partials (twice the
+    bytes when LL-packed), the residual and gamma (fp32) read; residual_out,
+    and y (bf16) and/or FP4 codes + scales written."""
+    P = plane_bytes(t, d)
+    reads = n * P * (2 if ll else 1) + P + 4 * d
+    writes = P + (P if out else 0) + ((t * d // 2 + t * d // 16) if fp4 else 0)
+    return reads, writes
+
+
+def counted_bytes(n: int, t: int, d: int) -> int:
+    """The workload's own counting: (N + 2) reads and 2 writes of t x d x 2."""
+    return (n + 2 + 2) * plane_bytes(t, d)
+
+
+def page_fused_bytes_per_token(d: int):
+    """Per-token traffic of the fused kernel as the TensorRT-LLM deep dive
+    (§6.4) accounts it: residual read, new residual and norm output written;
+    the peer slots it reads are not counted there."""
+    return 2 * d, 2 * 2 * d
+
+
+def page_unfused_bytes_per_token(d: int):
+    """Per-token traffic of the unfused path of the same table: the all-reduce
+    kernel reads and writes the tensor, then residual+norm reads two tensors
+    and writes two."""
+    return 3 * 2 * d, 3 * 2 * d
+
+
+def source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ------------------------------------------------------------ device helpers
+
+def _dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def dev_bf16(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(_dev()).view(torch.bfloat16)
+
+
+def dev_bytes(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(_dev())
+
+
+class PrefillSets:
+    """`nsets` device copies of one call's inputs plus outputs, rotated so
+    consecutive calls touch disjoint memory."""
+
+    def __init__(self, ci, nsets: int, fp4: bool = False, out: bool = True):
+        import torch
+        self.ci = ci
+        self.sets = []
+        parts0 = [dev_bf16(p) for p in ci.partials]
+        res0 = dev_bf16(ci.residual)
+        gamma = torch.from_numpy(ci.gamma).to(_dev())
+        for s in range(nsets):
+            parts = parts0 if s == 0 else [p.clone() for p in parts0]
+            res = res0 if s == 0 else res0.clone()
+            o = torch.empty_like(res0) if out else None
+            ro = torch.empty_like(res0)
+            codes = torch.empty((ci.t, ci.d // 2), dtype=torch.uint8, device=_dev()) if fp4 else None
+            scales = torch.empty((ci.t, ci.d // 16), dtype=torch.uint8, device=_dev()) if fp4 else None
+            self.sets.append((parts, res, gamma, o, ro, codes, scales))
+
+    def call(self, i: int):
+        import reduce_residual_rmsnorm_amd as arf
+        parts, res, gamma, o, ro, codes, scales = self.sets[i % len(self.sets)]
+        arf.arfuse_rmsnorm(parts, res, gamma, float(self.ci.eps), o, ro, codes, scales)
+
+
+def n_sets_for(call_bytes: int) -> int:
+    """Enough rotating sets that the bytes touched between two uses of a set
+    exceed twice the Infinity Cache."""
+    return max(2, math.ceil(2 * INFINITY_CACHE_BYTES / max(1, call_bytes)) + 1)
+
+
+def time_calls(fn, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` calls between two events on the
+    current stream, synchronized on both sides. Returns ms per call."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(steps):
+        fn(warmup + i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def time_graph(g, reps: int):
+    """p10/p50/p90 (µs) of `reps` replays of a captured graph, each bracketed
+    by its own events."""
+    import torch
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for s, e in ev:
+        s.record()
+        g.replay()
+        e.record()
+    torch.cuda.synchronize()
+    us = sorted(s.elapsed_time(e) * 1e3 for s, e in ev)
+    q = lambda p: us[min(len(us) - 1, int(p * len(us)))]
+    return dict(p10=q(0.1), p50=statistics.median(us), p90=q(0.9))
+
+
+# ------------------------------------------------------------ decode chains
+
+def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = False,
+                 out: bool = True, reps: int = 200, seed: int = 0):
+    """µs per call of a k-call chain captured in one graph (call c reads call
+    c-1's residual_out), and of the same-length graph of the empty kernel
+    with the same launch (the per-node floor)."""
+    import numpy as np
+    import torch
+
+    import reduce_residual_rmsnorm_amd as arf
+    import seeded_inputs as si
+
+    ci = si.make_call(n, t, d, seed=seed, outlier_frac=0.001 if fp4 else 0.0)
+    flags = [ci.ll_base + c for c in range(k)]
+    if ll:
+        # each call reads its own LL buffers carrying its own step flag
+        packed = np.stack([si.ll_pack_all(ci.partials, f) for f in flags])
+        pdev = dev_bytes(packed)
+        parts = [[pdev[c, i] for i in range(n)] for c in range(k)]
+    else:
+        p = [dev_bf16(x) for x in ci.partials]
+        parts = [p] * k
+    res0 = dev_bf16(ci.residual)
+    bufs = [torch.empty_like(res0), torch.empty_like(res0)]
+    gamma = torch.from_numpy(ci.gamma).to(_dev())
+    o = torch.empty_like(res0) if out else None
+    codes = torch.empty((t, d // 2), dtype=torch.uint8, device=_dev()) if fp4 else None
+    scales = torch.empty((t, d // 16), dtype=torch.uint8, device=_dev()) if fp4 else None
+    status = torch.zeros(4, dtype=torch.int32, device=_dev())
+    epi = (arf.ARFUSE_EPI_BF16 if out else 0) | (arf.ARFUSE_EPI_FP4 if fp4 else 0)
+
+    def enqueue():
+        for c in range(k):
+            rin = res0 if c == 0 else bufs[c % 2]
+            rout = bufs[(c + 1) % 2]
+            if ll:
+                arf.arfuse_rmsnorm_ex(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales,
+                                      layout=arf.ARFUSE_LAYOUT_LL, ll_flag=flags[c], max_polls=4,
+                                      status=status)
+            else:
+                arf.arfuse_rmsnorm(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales)
+
+    def enqueue_floor():
+        for _ in range(k):
+            arf.arfuse_launch_floor(n, t, d, epi, layout=arf.ARFUSE_LAYOUT_LL if ll else 0)
+
+    enqueue()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        enqueue()
+    gf = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gf):
+        enqueue_floor()
+    chain = time_graph(g, reps)
+    floor = time_graph(gf, reps)
+    st = status.cpu().numpy().view(np.uint32)
+    if ll and st[0] != 0:
+        raise RuntimeError("LL flags reported bad during the benchmark: %s" % st)
+    info = arf.arfuse_query_launch(n, t, d, epi)
+    r = dict(n=n, t=t, d=d, calls=k, layout="ll" if ll else "plain", fp4=fp4,
+             grid=int(info.grid), block=int(info.block),
+             us_per_call_p50=chain["p50"] / k, chain_us_p50=chain["p50"],
+             chain_us_p10=chain["p10"], chain_us_p90=chain["p90"],
+             floor_us_per_node_p50=floor["p50"] / k, floor_chain_us_p50=floor["p50"])
+    r["ratio_to_floor"] = r["us_per_call_p50"] / r["floor_us_per_node_p50"]
+    del g, gf
+    return r
+
+
+def prefill_gbps(n: int, t: int, d: int, steps: int, warmup: int, fp4=False, out=True, seed=0):
+    import seeded_inputs as si
+    ci = si.make_call(n, t, d, seed=seed, outlier_frac=0.001)
+    rd, wr = algorithmic_bytes(n, t, d, out=out, fp4=fp4)
+    sets = PrefillSets(ci, n_sets_for(rd + wr), fp4=fp4, out=out)
+    ms = time_calls(sets.call, steps, warmup)
+    r = dict(n=n, t=t, d=d, fp4=fp4, out=out, nsets=len(sets.sets), us_per_call=ms * 1e3,
+             algorithmic_gbps=(rd + wr) / (ms * 1e-3) / 1e9)
+    if not fp4:
+        r["counted_gbps"] = counted_bytes(n, t, d) / (ms * 1e-3) / 1e9
+    del sets
+    return r
+
+
+def stream_copy_gbps(nbytes: int = 1 << 30, steps: int = 20):
+    import torch
+
+    import reduce_residual_rmsnorm_amd as arf
+    a = torch.empty(nbytes, dtype=torch.uint8, device=_dev())
+    b = torch.empty(nbytes, dtype=torch.uint8, device=_dev())
+    a.fill_(1)
+    ms = time_calls(lambda i: arf.arfuse_stream_copy(b if i % 2 == 0 else a,
+                                                     a if i % 2 == 0 else b, nbytes),
+                    steps, 3)
+    return dict(bytes=nbytes, us=ms * 1e3, gbps=2 * nbytes / (ms * 1e-3) / 1e9)
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(ci, budget_s: float = 12.0):
+    """The oracle (scalar C, one host thread) on full calls of the timed
+    workload, repeated until about `budget_s` seconds; median time."""
+    import oracle
+    orc = oracle.default()
+    times = []
+    t_end = time.time() + budget_s
+    while time.time() < t_end or len(times) < 3:
+        t0 = time.perf_counter()
+        orc.allreduce_rmsnorm(ci.partials, ci.residual, ci.gamma, ci.eps)
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 50:
+            break
+    med = statistics.median(times)
+    return dict(value=counted_bytes(ci.n, ci.t, ci.d) / med / 1e9, unit="GB/s", cores=1,
+                kind="oracle",
+                sample="%d full calls of n=%d t=%d d=%d on one host thread (median %.3f s/call; "
+                       "host %s)" % (len(times), ci.n, ci.t, ci.d, med, _cpu_model()))
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ------------------------------------------------------------ traffic
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel source."""
+    path = os.path.join(PROFILES, "row_kernel_%s_traffic.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_digest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+# ------------------------------------------------------------ main
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extras", action="store_true", help="only the timed prefill workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only run the streaming-copy reference (counter calibration)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    import reduce_residual_rmsnorm_amd as arf
+    import seeded_inputs as si
+
+    if args.copy_only:
+        r = stream_copy_gbps()
+        print(json.dumps(dict(stream_copy=r)), flush=True)
+        return 0
+
+    name = "prefill_n8_t4096_d8192"
+    log("generating %s" % name)
+    ci = si.make_workload(name)
+    n, t, d = ci.n, ci.t, ci.d
+    rd, wr = algorithmic_bytes(n, t, d)
+    sets = PrefillSets(ci, n_sets_for(rd + wr))
+    info = arf.arfuse_query_launch(n, t, d, arf.ARFUSE_EPI_BF16)
+    log("timing %d steps after %d warmup (%d rotating sets, grid %d x block %d)"
+        % (args.steps, args.warmup, len(sets.sets), info.grid, info.block))
+    ms = time_calls(sets.call, args.steps, args.warmup)
+    value = counted_bytes(n, t, d) / (ms * 1e-3) / 1e9
+    achieved = (rd + wr) / (ms * 1e-3) / 1e9
+    log("%.2f us/call, %.0f GB/s counted, %.0f GB/s algorithmic" % (ms * 1e3, value, achieved))
+    del sets
+    torch.cuda.empty_cache()
+
+    extras = {}
+    if not args.no_extras:
+        log("stream copy reference")
+        extras["stream_copy_1GiB"] = stream_copy_gbps()
+        log("prefill t=512")
+        extras["prefill_n8_t512_d8192"] = prefill_gbps(8, 512, 8192, 100, 10)
+        log("fp4 t=512")
+        extras["fp4_n4_t512_d8192"] = prefill_gbps(4, 512, 8192, 100, 10, fp4=True, out=False)
+        for (nn, tt, dd, kk, ll, fp4, label) in [
+                (2, 1, 4096, 100, False, False, "decode_n2_t1_d4096_x100"),
+                (8, 8, 4096, 64, False, False, "decode_n8_t8_d4096_chain64"),
+                (4, 8, 8192, 160, False, False, "decode_n4_t8_d8192_chain160"),
+                (8, 8, 8192, 160, False, False, "decode_n8_t8_d8192_chain160"),
+                (4, 8, 8192, 160, True, False, "decode_n4_t8_d8192_chain160_ll"),
+                (8, 8, 8192, 160, True, False, "decode_n8_t8_d8192_chain160_ll"),
+                (4, 1, 8192, 100, False, True, "fp4_n4_t1_d8192_x100"),
+                (4, 8, 8192, 100, False, True, "fp4_n4_t8_d8192_x100"),
+                (4, 64, 8192, 100, False, True, "fp4_n4_t64_d8192_x100")]:
+            log("decode %s" % label)
+            extras[label] = decode_chain(nn, tt, dd, kk, ll=ll, fp4=fp4, out=not fp4)
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(ci)
+
+    traffic = recorded_traffic(name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "dtype_detail": "bf16 storage; fp32 rank-ordered sum and residual add; fp64 RMS and scaling",
+        "data": "synthetic (seeded N(0,1)/sqrt(N) partials, N(0,1) residual with 0.1% x100 rows, "
+                "U(0.5,1.5) gamma)",
+        "config": {"workload": name, "n_partials": n, "tokens": t, "hidden": d,
+                   "pct_of_peak_counted": round(100 * value / PEAK_HBM_GBPS, 1),
+                   "bytes_counted_per_step": counted_bytes(n, t, d),
+                   "bytes_algorithmic_per_step": rd + wr,
+                   "launch": {"grid": int(info.grid), "block": int(info.block),
+                              "vpt": int(info.vpt)}},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "kernel_source": source_digest(),
+        "extras": extras,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,204 @@
+/*
+ * arfuse — the epilogue of a one-shot all-reduce fused with the residual add,
+ * RMSNorm and an optional block-scaled FP4 quantization, for AMD Instinct
+ * MI355X (gfx950). C ABI.
+ *
+ * The operation (per token row r, column j; N rank partials p_0..p_{N-1}):
+ *
+ *   acc       = p_0 + p_1 + ... + p_{N-1}     fp32, in this rank order
+ *   h         = acc + residual                 fp32, residual added last
+ *   residual_out = bf16(h)                      round to nearest even
+ *   y         = h / sqrt(mean_j(h^2) + eps) * gamma_j
+ *   out       = bf16(y)                         optional
+ *   FP4       = per 16 consecutive elements of y: scale s = E4M3(max|y| / 6),
+ *               code = sign | E2M1(|y| / s)     optional
+ *
+ * Where the pages define it:
+ *  - The all-reduce of tensor parallelism sums same-shaped partial products of
+ *    the row-parallel layer ("Optimizing Tensor Parallelism Communication
+ *    Overhead ...", "The Anatomy of the Tensor Parallelism Bottleneck";
+ *    "Deep Dive: AllReduce and AllReduce Fusion in TensorRT-LLM", §2.1.1 and
+ *    §2.7). Here the N partials are N buffers in this GPU's HBM; they stand in
+ *    for the peer slots a one-shot kernel reads after the push (Deep Dive
+ *    §5.2, ONESHOT).
+ *  - A fixed summation order gives the same bits on every rank
+ *    ("Collectives, topology, custom all-reduce", the one-shot kernel and the
+ *    determinism section); fp32 accumulation is the fp32_acc option of the
+ *    fused call in the same page and the Fp32Acc template flag (Deep Dive
+ *    §3.1.5).
+ *  - Residual add, residual store, RMSNorm with gamma and eps, normalized
+ *    store and quantization follow the fused operator of Deep Dive §6.3 and
+ *    §6.5; eps is the layer norm's variance epsilon (Deep Dive §6.2).
+ *  - The LL layout (8 bytes of payload and an 8-byte flag in one 16-byte word,
+ *    the reader checking the flag) is the LL protocol of "Every µs Matters",
+ *    section on signalling without barriers.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked (device) are HIP device pointers; (host) are host memory.
+ *  - bf16 tensors are row-major [t][d] arrays of 16-bit bfloat16.
+ *  - The caller owns every buffer. The library allocates no memory, keeps no
+ *    pointer after it returns and holds no global state; calls are reentrant.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *    work; they never synchronize, so they are legal under stream capture.
+ *  - Argument errors are returned before anything is enqueued. A failed
+ *    launch returns ARFUSE_ERR_LAUNCH. Data-dependent errors (LL flags) are
+ *    written to a device status word instead (arfuse_ll_status).
+ *  - t == 0 is a no-op: only the shape, eps and the options are validated and
+ *    the buffer pointers may be NULL.
+ */
+#ifndef ARFUSE_H
+#define ARFUSE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ARFUSE_VERSION 1
+
+/* Largest supported rank count and row width. */
+#define ARFUSE_MAX_PARTIALS 8
+#define ARFUSE_MAX_D 65536
+
+typedef enum {
+  ARFUSE_OK = 0,
+  /* null or misaligned pointer, n_partials outside [1, 8], t < 0, d <= 0,
+   * d % 16 != 0, eps negative or not finite, overlapping buffers (other than
+   * residual_out == residual), bad option values */
+  ARFUSE_ERR_INVALID_ARG = 1,
+  /* valid arguments without a compiled kernel (d > ARFUSE_MAX_D, a launch
+   * override that does not cover the row) */
+  ARFUSE_ERR_UNSUPPORTED = 2,
+  /* the HIP runtime refused the launch */
+  ARFUSE_ERR_LAUNCH = 3,
+  /* device side only (arfuse_ll_status.code): some LL word still carried a
+   * flag other than the expected one after max_polls re-reads */
+  ARFUSE_ERR_FLAG_TIMEOUT = 4
+} arfuse_status;
+
+/* Input layouts of the partials. */
+#define ARFUSE_LAYOUT_PLAIN 0 /* bf16 [t][d], t*d*2 bytes per partial */
+#define ARFUSE_LAYOUT_LL 1    /* [t][d/4] 16-byte words: bytes 0..7 hold four
+                                 bf16 elements (element 4w first, little
+                                 endian), bytes 8..15 a little-endian uint64
+                                 flag; t*d*4 bytes per partial */
+
+/* Outputs of one call (the epilogue), as bit flags. */
+#define ARFUSE_EPI_BF16 1 /* out: bf16 y */
+#define ARFUSE_EPI_FP4 2  /* fp4_out + fp4_scales */
+
+/* Device-side status of an LL call. The caller zeroes it before the call
+ * (the library only ever ORs into code and adds to bad_words, so one word
+ * can collect several calls, e.g. a captured chain). */
+typedef struct {
+  uint32_t code;      /* 0, or ARFUSE_ERR_FLAG_TIMEOUT */
+  uint32_t reserved;
+  uint64_t bad_words; /* LL words whose flag never matched */
+} arfuse_ll_status;
+
+/* Options of arfuse_rmsnorm_ex. Zero-initialise it for the defaults
+ * (plain layout, library-chosen launch). */
+typedef struct {
+  int32_t layout;             /* ARFUSE_LAYOUT_PLAIN or ARFUSE_LAYOUT_LL */
+  uint32_t max_polls;         /* LL: re-reads of a word whose flag does not
+                                 match, with a short sleep between them,
+                                 before it counts as bad (0: check once) */
+  uint64_t ll_flag;           /* LL: the flag every word must carry */
+  arfuse_ll_status* status;   /* LL: (device) status word, or NULL */
+  int32_t block_threads;      /* launch override: threads per row block,
+                                 a multiple of 64 in [64, 1024]; 0 = auto */
+  int32_t vpt;                /* launch override: 16-byte vectors per thread
+                                 per partial, 1, 2, 4 or 8; 0 = auto */
+} arfuse_opts;
+
+/* The launch the library would use for a call. */
+typedef struct {
+  int64_t grid;         /* workgroups (one token row each) */
+  int32_t block;        /* threads per workgroup */
+  int32_t vpt;          /* 16-byte vectors per thread per partial */
+} arfuse_launch_info;
+
+/*
+ * arfuse_rmsnorm — the fused call on plain-layout partials.
+ *
+ *  partials      (host) array of n_partials pointers; each (device) bf16
+ *                [t][d], 16-byte aligned. Summed in array order.
+ *  n_partials    1..8
+ *  residual      (device) bf16 [t][d], 16-byte aligned
+ *  gamma         (device) fp32 [d], 16-byte aligned
+ *  eps           finite, >= 0; added to the mean square inside the root
+ *  out           (device) bf16 [t][d] normalized output, 16-byte aligned;
+ *                may be NULL only when fp4_out is given
+ *  residual_out  (device) bf16 [t][d] = bf16(h); may equal residual (in place)
+ *                but must not otherwise overlap any other buffer
+ *  fp4_out       (device) uint8 [t][d/2] E2M1 codes, element 2k in the low
+ *                nibble of byte k; 16-byte aligned; or NULL
+ *  fp4_scales    (device) uint8 [t][d/16] E4M3 codes of the block scales;
+ *                NULL exactly when fp4_out is NULL
+ *  t, d          rows (tokens) and row width; d % 16 == 0, d <= 65536
+ *  stream        hipStream_t
+ * Returns an arfuse_status.
+ */
+int arfuse_rmsnorm(const void* const* partials, int n_partials, const void* residual,
+                   const float* gamma, float eps, void* out, void* residual_out,
+                   uint8_t* fp4_out, uint8_t* fp4_scales, int64_t t, int64_t d,
+                   void* stream);
+
+/*
+ * arfuse_rmsnorm_ex — as arfuse_rmsnorm, with options (opts may be NULL).
+ * With opts->layout == ARFUSE_LAYOUT_LL every partial is (device) LL words
+ * [t][d/4][16 bytes]; each word's flag is compared with opts->ll_flag and a
+ * word that does not match is re-read up to opts->max_polls times. Words that
+ * never match are counted into opts->status (if given); the rows holding
+ * them get unspecified outputs. The kernel never waits without bound.
+ */
+int arfuse_rmsnorm_ex(const void* const* partials, int n_partials, const void* residual,
+                      const float* gamma, float eps, void* out, void* residual_out,
+                      uint8_t* fp4_out, uint8_t* fp4_scales, int64_t t, int64_t d,
+                      void* stream, const arfuse_opts* opts);
+
+/*
+ * arfuse_quantize_fp4 — the FP4 epilogue alone, on fp32 y [t][d] (device,
+ * 16-byte aligned), with the same device code as the fused call. codes:
+ * (device) uint8 [t][d/2], 16-byte aligned; scales: (device) uint8 [t][d/16].
+ * d % 16 == 0. (Deep Dive §6.5: quantization of the normalized output.)
+ */
+int arfuse_quantize_fp4(const float* y, int64_t t, int64_t d, uint8_t* codes,
+                        uint8_t* scales, void* stream);
+
+/*
+ * arfuse_query_launch — fill *info with the launch a call with these
+ * arguments would use. Host only, enqueues nothing. epilogue is a mask of
+ * ARFUSE_EPI_* flags. Returns an arfuse_status.
+ */
+int arfuse_query_launch(int n_partials, int64_t t, int64_t d, int epilogue,
+                        const arfuse_opts* opts, arfuse_launch_info* info);
+
+/*
+ * arfuse_launch_floor — measurement aid: enqueue an empty kernel with the
+ * same grid, block and argument block as the fused call would use, to
+ * measure the per-launch floor (a single launch or a node of a captured
+ * chain). Returns an arfuse_status.
+ */
+int arfuse_launch_floor(int n_partials, int64_t t, int64_t d, int epilogue,
+                        const arfuse_opts* opts, void* stream);
+
+/*
+ * arfuse_stream_copy — measurement aid: copy `bytes` (a multiple of 16) from
+ * src to dst (device, 16-byte aligned, not overlapping) with the same
+ * 16-byte streaming loads and stores the fused kernel uses; a reference for
+ * achievable HBM bandwidth and for scaling hardware byte counters.
+ */
+int arfuse_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+/* Static description of a status code. */
+const char* arfuse_status_string(int status);
+
+/* ARFUSE_VERSION of the built library. */
+int arfuse_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ARFUSE_H */

@@ -1,0 +1,190 @@
+"""Python binding of the arfuse C ABI (include/arfuse.h): argument marshalling
+only. Every step of the fused call runs in the gfx950 kernels of
+``lib/libarfuse.so``; PyTorch provides device memory and streams.
+
+Build the library first (``python -m reduce_residual_rmsnorm_amd.build`` or
+``__graft_entry__.build()``); importing this package without it fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libarfuse.so")
+
+ARFUSE_OK = 0
+ARFUSE_ERR_INVALID_ARG = 1
+ARFUSE_ERR_UNSUPPORTED = 2
+ARFUSE_ERR_LAUNCH = 3
+ARFUSE_ERR_FLAG_TIMEOUT = 4
+ARFUSE_LAYOUT_PLAIN = 0
+ARFUSE_LAYOUT_LL = 1
+ARFUSE_EPI_BF16 = 1
+ARFUSE_EPI_FP4 = 2
+ARFUSE_MAX_PARTIALS = 8
+ARFUSE_MAX_D = 65536
+
+# The exported functions, as declared in include/arfuse.h.
+EXPORTED = ("arfuse_rmsnorm", "arfuse_rmsnorm_ex", "arfuse_quantize_fp4", "arfuse_query_launch",
+            "arfuse_launch_floor", "arfuse_stream_copy", "arfuse_status_string", "arfuse_version")
+
+
+class ArfuseError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s: %s (status %d)" % (where, arfuse_status_string(code), code))
+
+
+class arfuse_ll_status(ctypes.Structure):
+    _fields_ = [("code", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("bad_words", ctypes.c_uint64)]
+
+
+class arfuse_opts(ctypes.Structure):
+    _fields_ = [("layout", ctypes.c_int32), ("max_polls", ctypes.c_uint32),
+                ("ll_flag", ctypes.c_uint64), ("status", ctypes.c_void_p),
+                ("block_threads", ctypes.c_int32), ("vpt", ctypes.c_int32)]
+
+
+class arfuse_launch_info(ctypes.Structure):
+    _fields_ = [("grid", ctypes.c_int64), ("block", ctypes.c_int32), ("vpt", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libarfuse.so is not built (%s); run `python -m "
+                          "reduce_residual_rmsnorm_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    common = [P, I, P, P, ctypes.c_float, P, P, P, P, I64, I64, P]
+    lib.arfuse_rmsnorm.argtypes = common
+    lib.arfuse_rmsnorm.restype = I
+    lib.arfuse_rmsnorm_ex.argtypes = common + [ctypes.POINTER(arfuse_opts)]
+    lib.arfuse_rmsnorm_ex.restype = I
+    lib.arfuse_quantize_fp4.argtypes = [P, I64, I64, P, P, P]
+    lib.arfuse_quantize_fp4.restype = I
+    lib.arfuse_query_launch.argtypes = [I, I64, I64, I, ctypes.POINTER(arfuse_opts),
+                                        ctypes.POINTER(arfuse_launch_info)]
+    lib.arfuse_query_launch.restype = I
+    lib.arfuse_launch_floor.argtypes = [I, I64, I64, I, ctypes.POINTER(arfuse_opts), P]
+    lib.arfuse_launch_floor.restype = I
+    lib.arfuse_stream_copy.argtypes = [P, P, I64, P]
+    lib.arfuse_stream_copy.restype = I
+    lib.arfuse_status_string.argtypes = [I]
+    lib.arfuse_status_string.restype = ctypes.c_char_p
+    lib.arfuse_version.argtypes = []
+    lib.arfuse_version.restype = I
+    return lib
+
+
+lib = _load()
+
+
+# ---------------------------------------------------------------- marshalling
+
+def _addr(x) -> int:
+    """Device address of a tensor, or an int address, or 0 for None."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _opts(layout=ARFUSE_LAYOUT_PLAIN, ll_flag=0, max_polls=0, status=None, block_threads=0,
+          vpt=0) -> arfuse_opts:
+    return arfuse_opts(layout=int(layout), max_polls=int(max_polls), ll_flag=int(ll_flag),
+                       status=_addr(status), block_threads=int(block_threads), vpt=int(vpt))
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != ARFUSE_OK:
+        raise ArfuseError(rc, where)
+
+
+def _td(residual, t, d):
+    if t is None or d is None:
+        t, d = residual.shape
+    return int(t), int(d)
+
+
+# ---------------------------------------------------------------- entry points
+
+def arfuse_rmsnorm(partials: Sequence, residual, gamma, eps: float, out, residual_out,
+                   fp4_out=None, fp4_scales=None, stream=None, t=None, d=None) -> None:
+    """Fused call on plain bf16 partials; see arfuse_rmsnorm in include/arfuse.h.
+    Tensors (or int device addresses with explicit t, d) are passed through."""
+    t, d = _td(residual, t, d)
+    arr = (ctypes.c_void_p * len(partials))(*[_addr(p) for p in partials])
+    rc = lib.arfuse_rmsnorm(arr, len(partials), _addr(residual), _addr(gamma), float(eps),
+                            _addr(out), _addr(residual_out), _addr(fp4_out), _addr(fp4_scales),
+                            t, d, _stream(stream))
+    _check(rc, "arfuse_rmsnorm")
+
+
+def arfuse_rmsnorm_ex(partials: Sequence, residual, gamma, eps: float, out, residual_out,
+                      fp4_out=None, fp4_scales=None, stream=None, t=None, d=None, *,
+                      layout=ARFUSE_LAYOUT_PLAIN, ll_flag=0, max_polls=0, status=None,
+                      block_threads=0, vpt=0) -> None:
+    """Fused call with options; see arfuse_rmsnorm_ex in include/arfuse.h."""
+    t, d = _td(residual, t, d)
+    arr = (ctypes.c_void_p * len(partials))(*[_addr(p) for p in partials])
+    o = _opts(layout, ll_flag, max_polls, status, block_threads, vpt)
+    rc = lib.arfuse_rmsnorm_ex(arr, len(partials), _addr(residual), _addr(gamma), float(eps),
+                               _addr(out), _addr(residual_out), _addr(fp4_out),
+                               _addr(fp4_scales), t, d, _stream(stream), ctypes.byref(o))
+    _check(rc, "arfuse_rmsnorm_ex")
+
+
+def arfuse_quantize_fp4(y, codes, scales, stream=None, t=None, d=None) -> None:
+    """FP4 epilogue alone on fp32 y [t][d]; see include/arfuse.h."""
+    if t is None or d is None:
+        t, d = y.shape
+    rc = lib.arfuse_quantize_fp4(_addr(y), int(t), int(d), _addr(codes), _addr(scales),
+                                 _stream(stream))
+    _check(rc, "arfuse_quantize_fp4")
+
+
+def arfuse_query_launch(n_partials: int, t: int, d: int, epilogue: int = ARFUSE_EPI_BF16,
+                        **opts) -> arfuse_launch_info:
+    info = arfuse_launch_info()
+    o = _opts(**opts)
+    rc = lib.arfuse_query_launch(int(n_partials), int(t), int(d), int(epilogue),
+                                 ctypes.byref(o), ctypes.byref(info))
+    _check(rc, "arfuse_query_launch")
+    return info
+
+
+def arfuse_launch_floor(n_partials: int, t: int, d: int, epilogue: int = ARFUSE_EPI_BF16,
+                        stream=None, **opts) -> None:
+    o = _opts(**opts)
+    rc = lib.arfuse_launch_floor(int(n_partials), int(t), int(d), int(epilogue),
+                                 ctypes.byref(o), _stream(stream))
+    _check(rc, "arfuse_launch_floor")
+
+
+def arfuse_stream_copy(dst, src, nbytes: Optional[int] = None, stream=None) -> None:
+    if nbytes is None:
+        nbytes = src.numel() * src.element_size()
+    rc = lib.arfuse_stream_copy(_addr(dst), _addr(src), int(nbytes), _stream(stream))
+    _check(rc, "arfuse_stream_copy")
+
+
+def arfuse_status_string(code: int) -> str:
+    return lib.arfuse_status_string(int(code)).decode()
+
+
+def arfuse_version() -> int:
+    return lib.arfuse_version()

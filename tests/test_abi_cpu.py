@@ -1,0 +1,168 @@
+"""C-ABI library: loads, exports every declared symbol, and validates its
+arguments on the host before any HIP call (no GPU needed: every call here
+either returns an argument error or is a t == 0 no-op)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import reduce_residual_rmsnorm_amd as arf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "arfuse.h")
+
+# fake, 16-byte aligned, never dereferenced device addresses
+A = [0x10000 * (i + 1) for i in range(16)]
+T, D = 8, 4096
+PLANE = T * D * 2
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+(arfuse_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_exported_set():
+    assert declared_functions() == sorted(arf.EXPORTED)
+
+
+@pytest.mark.parametrize("name", sorted(arf.EXPORTED))
+def test_symbol_exported(name):
+    lib = ctypes.CDLL(arf.LIB_PATH)
+    assert hasattr(lib, name)
+
+
+def test_version_and_status_strings():
+    assert arf.arfuse_version() == 1
+    for code in range(5):
+        assert arf.arfuse_status_string(code)
+    assert arf.arfuse_status_string(99) == "unknown status"
+
+
+def call(parts=None, n=None, residual=None, gamma=None, eps=1e-5, out=None, residual_out=None,
+         fp4=None, scales=None, t=T, d=D, opts=None):
+    parts = list(A[:4]) if parts is None else parts
+    n = len(parts) if n is None else n
+    arr = (ctypes.c_void_p * max(1, len(parts)))(*parts) if parts else None
+    args = [arr, n, A[8] * 16 if residual is None else residual,
+            A[9] * 16 if gamma is None else gamma, eps,
+            A[10] * 16 if out is None else out,
+            A[11] * 16 if residual_out is None else residual_out, fp4 or 0, scales or 0, t, d, 0]
+    if opts is None:
+        return arf.lib.arfuse_rmsnorm(*args)
+    return arf.lib.arfuse_rmsnorm_ex(*args, ctypes.byref(opts))
+
+
+BIG = 1 << 32  # spacing that keeps the fake buffers of a [8][4096] call apart
+
+
+def spaced(i):
+    return BIG * (i + 1)
+
+
+def good(**kw):
+    base = dict(parts=[spaced(i) for i in range(4)], residual=spaced(8), gamma=spaced(9),
+                out=spaced(10), residual_out=spaced(11))
+    base.update(kw)
+    return base
+
+
+INVALID = {
+    "no_partials_array": dict(parts=[], n=1),
+    "n_zero": dict(n=0),
+    "n_nine": dict(parts=[spaced(i) for i in range(9)]),
+    "null_partial": dict(parts=[spaced(0), 0]),
+    "misaligned_partial": dict(parts=[spaced(0) + 8]),
+    "null_residual": dict(residual=0),
+    "null_gamma": dict(gamma=0),
+    "null_residual_out": dict(residual_out=0),
+    "no_output": dict(out=0),
+    "misaligned_out": dict(out=spaced(10) + 4),
+    "fp4_without_scales": dict(fp4=spaced(12)),
+    "scales_without_fp4": dict(scales=spaced(13)),
+    "negative_t": dict(t=-1),
+    "zero_d": dict(d=0),
+    "d_not_multiple_of_16": dict(d=4104),
+    "negative_eps": dict(eps=-1e-5),
+    "nan_eps": dict(eps=float("nan")),
+    "inf_eps": dict(eps=float("inf")),
+    "out_is_partial": dict(out=spaced(1)),
+    "residual_out_is_partial": dict(residual_out=spaced(2)),
+    "out_is_residual": dict(out=spaced(8)),
+    "out_overlaps_residual_out": dict(out=spaced(11) + PLANE - 16),
+    "residual_out_overlaps_residual": dict(residual_out=spaced(8) + 16),
+    "out_overlaps_gamma": dict(out=spaced(9) - PLANE + 16),
+    "fp4_overlaps_out": dict(fp4=spaced(10) + 16, scales=spaced(13)),
+    "scales_overlap_fp4": dict(fp4=spaced(12), scales=spaced(12) + 16),
+}
+
+
+@pytest.mark.parametrize("case", sorted(INVALID))
+def test_invalid_arguments_rejected(case):
+    assert call(**good(**INVALID[case])) == arf.ARFUSE_ERR_INVALID_ARG
+
+
+def test_unsupported_width():
+    assert call(**good(d=65536 + 16)) == arf.ARFUSE_ERR_UNSUPPORTED
+
+
+def test_t_zero_is_a_noop():
+    assert call(**good(t=0)) == arf.ARFUSE_OK
+    # buffers may be NULL (an empty tensor's data pointer) when t == 0
+    assert call(parts=[0, 0], residual=0, gamma=0, out=0, residual_out=0, t=0) == arf.ARFUSE_OK
+    assert call(**good(t=0, eps=-1.0)) == arf.ARFUSE_ERR_INVALID_ARG
+    assert call(**good(t=0, d=24)) == arf.ARFUSE_ERR_INVALID_ARG
+
+
+def test_bad_options_rejected():
+    o = arf._opts(layout=2)
+    assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
+    for bt in (32, 100, 2048):
+        assert call(**good(opts=arf._opts(block_threads=bt))) == arf.ARFUSE_ERR_INVALID_ARG
+    assert call(**good(opts=arf._opts(vpt=3))) == arf.ARFUSE_ERR_INVALID_ARG
+    # an override that cannot cover the row
+    assert call(**good(opts=arf._opts(block_threads=64, vpt=1))) == arf.ARFUSE_ERR_UNSUPPORTED
+
+
+def test_ll_partials_occupy_twice_the_bytes():
+    # plain partials one plane apart are fine; as LL they overlap each other's
+    # successor... only outputs are checked against inputs, so place out one
+    # plane after a partial: valid for plain, overlapping for LL.
+    kw = good(out=spaced(0) + PLANE)
+    assert call(**dict(kw, t=0)) == arf.ARFUSE_OK
+    o = arf._opts(layout=arf.ARFUSE_LAYOUT_LL)
+    assert call(**dict(kw, opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("d,block,vpt", [(16, 64, 1), (4096, 512, 1), (8192, 1024, 1),
+                                         (8208, 576, 2), (16384, 1024, 2), (65536, 1024, 8),
+                                         (48, 64, 1)])
+def test_query_launch_auto(d, block, vpt):
+    info = arf.arfuse_query_launch(8, 5, d)
+    assert (info.grid, info.block, info.vpt) == (5, block, vpt)
+    assert info.block * info.vpt * 8 >= d
+
+
+def test_query_launch_override():
+    info = arf.arfuse_query_launch(8, 3, 8192, block_threads=512)
+    assert (info.block, info.vpt) == (512, 2)
+    info = arf.arfuse_query_launch(8, 3, 8192, vpt=4)
+    assert (info.block, info.vpt) == (256, 4)
+
+
+def test_quantize_and_copy_validation():
+    q = arf.lib.arfuse_quantize_fp4
+    assert q(spaced(0), 4, 4104, spaced(1), spaced(2), 0) == arf.ARFUSE_ERR_INVALID_ARG
+    assert q(spaced(0) + 4, 4, 4096, spaced(1), spaced(2), 0) == arf.ARFUSE_ERR_INVALID_ARG
+    assert q(spaced(0), 4, 4096, spaced(0) + 16, spaced(2), 0) == arf.ARFUSE_ERR_INVALID_ARG
+    assert q(0, 4, 4096, spaced(1), spaced(2), 0) == arf.ARFUSE_ERR_INVALID_ARG
+    assert q(spaced(0), 0, 4096, spaced(1), spaced(2), 0) == arf.ARFUSE_OK
+    assert q(0, 0, 4096, 0, 0, 0) == arf.ARFUSE_OK
+    c = arf.lib.arfuse_stream_copy
+    assert c(spaced(0), spaced(1), 24, 0) == arf.ARFUSE_ERR_INVALID_ARG
+    assert c(spaced(0), spaced(0) + 16, 64, 0) == arf.ARFUSE_ERR_INVALID_ARG
+    assert c(spaced(0), spaced(1), 0, 0) == arf.ARFUSE_OK

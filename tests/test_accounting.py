@@ -1,0 +1,70 @@
+"""Host-side byte accounting of the benchmark against figures the pages print
+(tests/golden/page_figures.json), and the launch-independent bookkeeping of
+bench.py (no GPU)."""
+
+import json
+import os
+
+import pytest
+
+import bench
+
+G = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                "page_figures.json")))
+
+
+def test_message_sizes():
+    assert bench.plane_bytes(1, 8192) == G["bytes_per_token_d8192_bf16"]["value"]
+    assert bench.plane_bytes(8, 4096) == G["message_bytes_t8_d4096_bf16"]["value"]
+    assert bench.plane_bytes(8, 8192) == G["message_bytes_t8_d8192_16bit"]["value"]
+
+
+def test_ring_wire_bytes():
+    n, s = 8, bench.plane_bytes(8, 4096)
+    assert 2 * (n - 1) * s // n == G["ring_wire_bytes_n8_t8_d4096"]["value"]
+
+
+def test_fused_and_unfused_per_token():
+    r, w = bench.page_fused_bytes_per_token(8192)
+    g = G["fused_traffic_per_token_d8192"]
+    assert (r, w, r + w) == (g["reads"], g["writes"], g["total"])
+    r, w = bench.page_unfused_bytes_per_token(8192)
+    g = G["unfused_traffic_per_token_d8192"]
+    assert (r, w, r + w) == (g["reads"], g["writes"], g["total"])
+    saved = (sum(bench.page_unfused_bytes_per_token(8192)) -
+             sum(bench.page_fused_bytes_per_token(8192))) * 64 * 108 // 1024
+    assert saved == G["saved_per_forward_pass_kb_64tok_108layers"]["value"]
+
+
+def test_oneshot_twoshot_traffic():
+    n, D = 8, 2 << 20
+    g = G["oneshot_vs_twoshot_traffic_n8_D2MB"]
+    assert n * (n - 1) * D // (1 << 20) == g["oneshot_total_mb"]
+    assert 2 * (n - 1) * D // (1 << 20) == g["twoshot_total_mb"]
+
+
+def test_algorithmic_bytes_add_the_slot_reads():
+    # the page's fused figure plus the N partial reads and gamma
+    n, t, d = 8, 4096, 8192
+    rd, wr = bench.algorithmic_bytes(n, t, d)
+    pr, pw = bench.page_fused_bytes_per_token(d)
+    assert rd == t * pr + n * bench.plane_bytes(t, d) + 4 * d
+    assert wr == t * pw
+    assert rd + wr == 738230272
+    assert bench.counted_bytes(n, t, d) == 12 * 64 * (1 << 20)
+    rd, wr = bench.algorithmic_bytes(4, 512, 8192, out=False, fp4=True)
+    assert rd + wr == 52723712
+    rd, _ = bench.algorithmic_bytes(8, 8, 8192, ll=True)
+    assert rd == 8 * 2 * 131072 + 131072 + 4 * 8192
+
+
+@pytest.mark.parametrize("call_bytes,sets", [(738230272, 2), (92307456, 7), (1, 2 * 256 * 2 ** 20 + 1)])
+def test_rotation_defeats_infinity_cache(call_bytes, sets):
+    n = bench.n_sets_for(call_bytes)
+    assert n == sets
+    assert (n - 1) * call_bytes >= 2 * bench.INFINITY_CACHE_BYTES
+
+
+def test_bench_refuses_more_than_one_gpu(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
