@@ -70,7 +70,8 @@ typedef enum {
   /* valid arguments without a compiled kernel (d > ARFUSE_MAX_D, a launch
    * override that does not cover the row) */
   ARFUSE_ERR_UNSUPPORTED = 2,
-  /* the HIP runtime refused the launch */
+  /* the HIP runtime refused the launch; the returned value also carries the
+   * runtime's hipError_t in bits 8 and up (status & 0xFF == 3) */
   ARFUSE_ERR_LAUNCH = 3,
   /* device side only (arfuse_ll_status.code): some LL word still carried a
    * flag other than the expected one after max_polls re-reads */

@@ -34,8 +34,12 @@ EXPORTED = ("arfuse_rmsnorm", "arfuse_rmsnorm_ex", "arfuse_quantize_fp4", "arfus
 
 class ArfuseError(RuntimeError):
     def __init__(self, code: int, where: str):
-        self.code = code
-        super().__init__("%s: %s (status %d)" % (where, arfuse_status_string(code), code))
+        self.code = code & 0xFF
+        self.hip_error = code >> 8
+        msg = "%s: %s (status %d)" % (where, arfuse_status_string(code), self.code)
+        if self.hip_error:
+            msg += ", hipError_t %d" % self.hip_error
+        super().__init__(msg)
 
 
 class arfuse_ll_status(ctypes.Structure):
@@ -54,6 +58,12 @@ class arfuse_launch_info(ctypes.Structure):
 
 
 def _load():
+    # PyTorch's ROCm wheel carries its own HIP runtime (libamdhip64.so.7) and
+    # finds it by path. If libarfuse.so were loaded first it would pull in the
+    # system runtime under the same soname and the process would hold two HIP
+    # runtimes, each rejecting the other's streams. Importing torch first makes
+    # the dynamic linker bind libarfuse.so to the runtime torch already loaded.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError("libarfuse.so is not built (%s); run `python -m "
                           "reduce_residual_rmsnorm_amd.build`" % LIB_PATH)

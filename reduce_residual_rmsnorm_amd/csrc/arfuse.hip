@@ -371,6 +371,11 @@ RowFn select_row_kernel(int n, int vpt, bool ll, int epi) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// ARFUSE_ERR_LAUNCH carries the runtime's hipError_t in bits 8 and up.
+int launch_status(hipError_t e) {
+  return e == hipSuccess ? ARFUSE_OK : (ARFUSE_ERR_LAUNCH | ((int)e << 8));
+}
+
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
 };
@@ -490,7 +495,7 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
   void* args[] = {&a};
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)t), dim3((unsigned)block), args, 0,
                                  (hipStream_t)stream);
-  return e == hipSuccess ? ARFUSE_OK : ARFUSE_ERR_LAUNCH;
+  return launch_status(e);
 }
 
 }  // namespace
@@ -530,7 +535,7 @@ int arfuse_quantize_fp4(const float* y, int64_t t, int64_t d, uint8_t* codes, ui
   void* args[] = {&yy, &nv, &cc, &scales};
   hipError_t e = hipLaunchKernel((const void*)quant_kernel, dim3((unsigned)grid), dim3(256), args,
                                  0, (hipStream_t)stream);
-  return e == hipSuccess ? ARFUSE_OK : ARFUSE_ERR_LAUNCH;
+  return launch_status(e);
 }
 
 int arfuse_query_launch(int n_partials, int64_t t, int64_t d, int epilogue,
@@ -561,7 +566,7 @@ int arfuse_launch_floor(int n_partials, int64_t t, int64_t d, int epilogue,
   void* args[] = {&a};
   hipError_t e = hipLaunchKernel((const void*)floor_kernel, dim3((unsigned)t), dim3((unsigned)block),
                                  args, 0, (hipStream_t)stream);
-  return e == hipSuccess ? ARFUSE_OK : ARFUSE_ERR_LAUNCH;
+  return launch_status(e);
 }
 
 int arfuse_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) {
@@ -578,10 +583,11 @@ int arfuse_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) 
   void* args[] = {&s, &dd, &nn};
   hipError_t e = hipLaunchKernel((const void*)copy_kernel, dim3((unsigned)grid), dim3(256), args, 0,
                                  (hipStream_t)stream);
-  return e == hipSuccess ? ARFUSE_OK : ARFUSE_ERR_LAUNCH;
+  return launch_status(e);
 }
 
 const char* arfuse_status_string(int status) {
+  if ((status & 0xFF) == ARFUSE_ERR_LAUNCH) return "kernel launch failed";
   switch (status) {
     case ARFUSE_OK: return "ok";
     case ARFUSE_ERR_INVALID_ARG: return "invalid argument";

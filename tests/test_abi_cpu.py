@@ -166,3 +166,16 @@ def test_quantize_and_copy_validation():
     assert c(spaced(0), spaced(1), 24, 0) == arf.ARFUSE_ERR_INVALID_ARG
     assert c(spaced(0), spaced(0) + 16, 64, 0) == arf.ARFUSE_ERR_INVALID_ARG
     assert c(spaced(0), spaced(1), 0, 0) == arf.ARFUSE_OK
+
+
+def test_single_hip_runtime_in_process():
+    """Importing the binding first must not leave two HIP runtimes in the
+    process (PyTorch carries its own libamdhip64 under the same soname)."""
+    import subprocess
+    import sys
+    code = ("import reduce_residual_rmsnorm_amd, torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       check=True)
+    assert r.stdout.strip() == "1", r.stdout + r.stderr
