@@ -321,6 +321,88 @@ def recorded_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+# ------------------------------------------------------------ profile summaries
+
+PROFILE_COMMANDS = {
+    "trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
+             "-d $REPO/gpurun_out/prof_trace -o prefill -- python3 $REPO/bench.py --steps 50 "
+             "--warmup 5 --no-extras --no-cpu-baseline",
+    "pmc_prefill": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {C} --kernel-include-regex "
+                   "row_kernel -f csv -d $REPO/gpurun_out/pmc_prefill_{C} -o pmc -- python3 "
+                   "$REPO/bench.py --steps 5 --warmup 1 --no-extras --no-cpu-baseline",
+    "pmc_copy": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {C} --kernel-include-regex "
+                "copy_kernel -f csv -d $REPO/gpurun_out/pmc_copy_{C} -o pmc -- python3 "
+                "$REPO/bench.py --copy-only",
+}
+
+
+def _bench_line(log_path):
+    with open(log_path) as f:
+        for line in f:
+            if line.startswith("{"):
+                return json.loads(line)
+    return None
+
+
+def _counter(path, kname):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if kname in r["Kernel_Name"]]
+    return statistics.median(vals), len(vals)
+
+
+def summarize_profiles(outdir: str) -> None:
+    """Write profiles/row_kernel_<workload>_{stats.md,traffic.json} from the
+    rocprofv3 outputs of PROFILE_COMMANDS under `outdir` (gpurun_out/)."""
+    import csv
+    name = "prefill_n8_t4096_d8192"
+    os.makedirs(PROFILES, exist_ok=True)
+    line = _bench_line(os.path.join(outdir, "prof_trace.log"))
+    rows = list(csv.DictReader(open(os.path.join(outdir, "prof_trace", "prefill_kernel_stats.csv"))))
+    md = ["# row_kernel, %s: rocprofv3 kernel statistics" % name, "",
+          "Command (`$REPO` is the repository root):", "", "    " + PROFILE_COMMANDS["trace"], "",
+          "Kernel source sha256[:16]: `%s`" % (line or {}).get("kernel_source", "?"), "",
+          "| kernel | calls | average µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        md.append("| `%s` | %s | %.2f | %.2f | %.2f | %s |" % (
+            r["Name"].replace("(anonymous namespace)::", ""), r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, r["Percentage"]))
+    if line:
+        rd, wr = algorithmic_bytes(8, 4096, 8192)
+        md += ["", "The same run's bench line (HIP events over the %d timed calls): %.2f µs per call, "
+               "%.1f GB/s counted, roofline.achieved %.1f GB/s algorithmic (%.1f%% of 8 TB/s)." % (
+                   line["steps"], line["ms_per_step"] * 1e3, line["value"],
+                   line["roofline"]["achieved"], 100 * line["roofline"]["frac"])]
+    with open(os.path.join(PROFILES, "row_kernel_%s_stats.md" % name), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+    copy_bytes = 1 << 30
+    fetch, nf = _counter(os.path.join(outdir, "pmc_prefill_FETCH_SIZE", "pmc_counter_collection.csv"), "row_kernel")
+    write, nw = _counter(os.path.join(outdir, "pmc_prefill_WRITE_SIZE", "pmc_counter_collection.csv"), "row_kernel")
+    cfetch, _ = _counter(os.path.join(outdir, "pmc_copy_FETCH_SIZE", "pmc_counter_collection.csv"), "copy_kernel")
+    cwrite, _ = _counter(os.path.join(outdir, "pmc_copy_WRITE_SIZE", "pmc_counter_collection.csv"), "copy_kernel")
+    kf = copy_bytes / (cfetch * 1024)
+    kw = copy_bytes / (cwrite * 1024)
+    rd, wr = algorithmic_bytes(8, 4096, 8192)
+    pline = _bench_line(os.path.join(outdir, "pmc_prefill_FETCH_SIZE.log")) or {}
+    rec = {
+        "workload": name,
+        "source_sha256_16": pline.get("kernel_source"),
+        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write, "dispatches": [nf, nw],
+        "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_kib": cfetch, "write_kib": cwrite,
+                             "fetch_factor": kf, "write_factor": kw},
+        "read_bytes_per_launch": fetch * 1024 * kf, "write_bytes_per_launch": write * 1024 * kw,
+        "traffic_bytes_per_launch": round(fetch * 1024 * kf + write * 1024 * kw),
+        "algorithmic_read_bytes": rd, "algorithmic_write_bytes": wr,
+        "traffic_over_algorithmic": (fetch * 1024 * kf + write * 1024 * kw) / (rd + wr),
+        "commands": [PROFILE_COMMANDS["pmc_prefill"].format(C=c) for c in ("FETCH_SIZE", "WRITE_SIZE")] +
+                    [PROFILE_COMMANDS["pmc_copy"].format(C=c) for c in ("FETCH_SIZE", "WRITE_SIZE")],
+    }
+    with open(os.path.join(PROFILES, "row_kernel_%s_traffic.json" % name), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
 # ------------------------------------------------------------ main
 
 def main(argv=None):
@@ -332,7 +414,12 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the streaming-copy reference (counter calibration)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/ summaries from rocprofv3 outputs under DIR, then exit")
     args = ap.parse_args(argv)
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
