@@ -193,6 +193,13 @@ int arfuse_launch_floor(int n_partials, int64_t t, int64_t d, int epilogue,
  */
 int arfuse_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
 
+/*
+ * arfuse_round_bf16 — test entry: the fused kernel's fp32 -> bf16 rounding
+ * (round to nearest even) applied to x (device fp32 [n], 8-byte aligned),
+ * written to out (device bf16 bits [n], 4-byte aligned). n even.
+ */
+int arfuse_round_bf16(const float* x, int64_t n, uint16_t* out, void* stream);
+
 /* Static description of a status code. */
 const char* arfuse_status_string(int status);
 

@@ -2,7 +2,7 @@
 only. Every step of the fused call runs in the gfx950 kernels of
 ``lib/libarfuse.so``; PyTorch provides device memory and streams.
 
-Build the library first (``python -m reduce_residual_rmsnorm_amd.build`` or
+Build the library first (``python reduce_residual_rmsnorm_amd/build.py`` or
 ``__graft_entry__.build()``); importing this package without it fails.
 """
 
@@ -29,7 +29,8 @@ ARFUSE_MAX_D = 65536
 
 # The exported functions, as declared in include/arfuse.h.
 EXPORTED = ("arfuse_rmsnorm", "arfuse_rmsnorm_ex", "arfuse_quantize_fp4", "arfuse_query_launch",
-            "arfuse_launch_floor", "arfuse_stream_copy", "arfuse_status_string", "arfuse_version")
+            "arfuse_launch_floor", "arfuse_stream_copy", "arfuse_round_bf16",
+            "arfuse_status_string", "arfuse_version")
 
 
 class ArfuseError(RuntimeError):
@@ -57,17 +58,17 @@ class arfuse_launch_info(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_int64), ("block", ctypes.c_int32), ("vpt", ctypes.c_int32)]
 
 
-def _load():
+def _load(path: str = LIB_PATH):
     # PyTorch's ROCm wheel carries its own HIP runtime (libamdhip64.so.7) and
     # finds it by path. If libarfuse.so were loaded first it would pull in the
     # system runtime under the same soname and the process would hold two HIP
     # runtimes, each rejecting the other's streams. Importing torch first makes
     # the dynamic linker bind libarfuse.so to the runtime torch already loaded.
     import torch  # noqa: F401
-    if not os.path.exists(LIB_PATH):
-        raise ImportError("libarfuse.so is not built (%s); run `python -m "
-                          "reduce_residual_rmsnorm_amd.build`" % LIB_PATH)
-    lib = ctypes.CDLL(LIB_PATH)
+    if not os.path.exists(path):
+        raise ImportError("libarfuse.so is not built (%s); run `python "
+                          "reduce_residual_rmsnorm_amd/build.py`" % path)
+    lib = ctypes.CDLL(path)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     common = [P, I, P, P, ctypes.c_float, P, P, P, P, I64, I64, P]
     lib.arfuse_rmsnorm.argtypes = common
@@ -83,6 +84,8 @@ def _load():
     lib.arfuse_launch_floor.restype = I
     lib.arfuse_stream_copy.argtypes = [P, P, I64, P]
     lib.arfuse_stream_copy.restype = I
+    lib.arfuse_round_bf16.argtypes = [P, I64, P, P]
+    lib.arfuse_round_bf16.restype = I
     lib.arfuse_status_string.argtypes = [I]
     lib.arfuse_status_string.restype = ctypes.c_char_p
     lib.arfuse_version.argtypes = []
@@ -190,6 +193,12 @@ def arfuse_stream_copy(dst, src, nbytes: Optional[int] = None, stream=None) -> N
         nbytes = src.numel() * src.element_size()
     rc = lib.arfuse_stream_copy(_addr(dst), _addr(src), int(nbytes), _stream(stream))
     _check(rc, "arfuse_stream_copy")
+
+
+def arfuse_round_bf16(x, out, stream=None) -> None:
+    """Test entry: the kernel's fp32 -> bf16 rounding of x into out."""
+    rc = lib.arfuse_round_bf16(_addr(x), int(x.numel()), _addr(out), _stream(stream))
+    _check(rc, "arfuse_round_bf16")
 
 
 def arfuse_status_string(code: int) -> str:

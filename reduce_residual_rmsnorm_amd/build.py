@@ -1,6 +1,8 @@
 """Build the gfx950 shared library ``lib/libarfuse.so`` with hipcc, in-tree.
 
-    python -m reduce_residual_rmsnorm_amd.build
+    python reduce_residual_rmsnorm_amd/build.py
+
+(Run it as a file: importing the package loads the library it builds.)
 """
 
 from __future__ import annotations

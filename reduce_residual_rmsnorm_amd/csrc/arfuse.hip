@@ -28,8 +28,9 @@
 //    FMAs at the fp32 (non-packed) rate and this kernel is HBM-bound, so the
 //    extra precision costs no time and keeps y32 within an ulp of an fp64
 //    reference.
-//  * FP4 quantizes y32: s = E4M3(fl32(blockmax / 6)), q = fl32(|y| / s) with
-//    IEEE division, q rounded to the E2M1 grid with ties to the even code.
+//  * FP4 quantizes y32: s = E4M3(fl32(blockmax / 6)) (IEEE division), then
+//    |y| / s rounded to the E2M1 grid with ties to the even code, decided by
+//    exact comparisons with s * threshold (see e2m1_rne).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -40,6 +41,7 @@
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxBlock = 1024;
@@ -73,22 +75,20 @@ __device__ __forceinline__ void widen8(u32x4 r, float f[8]) {
   f[7] = __uint_as_float(r.w & 0xFFFF0000u);
 }
 
-// Round to nearest even for finite x: adding 0x7FFF plus the lowest kept bit
-// carries into the kept half exactly when the dropped half is above one half
-// of a bf16 ulp, or equal to it with an odd kept half.
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 -> two bf16, round to nearest even: gfx950's packed conversion
+// (v_cvt_pk_bf16_f32), one instruction per pair. Its rounding is checked
+// against the oracle on every tie and near-tie pattern of every 16-bit prefix
+// through arfuse_round_bf16.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ u32x4 narrow8(const float f[8]) {
-  u32x4 r;
-  r.x = bf16_rne(f[0]) | (bf16_rne(f[1]) << 16);
-  r.y = bf16_rne(f[2]) | (bf16_rne(f[3]) << 16);
-  r.z = bf16_rne(f[4]) | (bf16_rne(f[5]) << 16);
-  r.w = bf16_rne(f[6]) | (bf16_rne(f[7]) << 16);
-  return r;
+  return u32x4{pack_bf16(f[0], f[1]), pack_bf16(f[2], f[3]), pack_bf16(f[4], f[5]),
+               pack_bf16(f[6], f[7])};
 }
 
 // ------------------------------------------------------------- FP4 helpers
@@ -100,11 +100,11 @@ __device__ __forceinline__ u32x4 narrow8(const float f[8]) {
 // carry trick as bf16 (bit 20 is the lowest kept bit); the fp32 exponent
 // minus 120 is the E4M3 exponent field. Above 448 saturate.
 __device__ __forceinline__ uint32_t e4m3_rne(float x) {
-  if (x < 0.015625f) return (uint32_t)rintf(x * 512.0f);
+  const uint32_t sub = (uint32_t)rintf(x * 512.0f);
   uint32_t u = __float_as_uint(x);
   u += 0x7FFFFu + ((u >> 20) & 1u);
-  uint32_t c = (u >> 20) - (120u << 3);
-  return c > 0x7Eu ? 0x7Eu : c;
+  const uint32_t c = min((u >> 20) - (120u << 3), 0x7Eu);
+  return x < 0.015625f ? sub : c;
 }
 
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
@@ -112,13 +112,35 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return __uint_as_float((c + (120u << 3)) << 20);
 }
 
-// E2M1 magnitude code of q >= 0 (0, .5, 1, 1.5, 2, 3, 4, 6): a tie goes to
-// the even code, so ties at .25, 1.25, 2.5 and 5 round down and those at .75,
-// 1.75 and 3.5 round up; above 6 saturates.
-__device__ __forceinline__ uint32_t e2m1_rne(float q) {
-  return (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) +
-         (uint32_t)(q >= 1.75f) + (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) +
-         (uint32_t)(q > 5.0f);
+// E2M1 magnitude code (0, .5, 1, 1.5, 2, 3, 4, 6 -> 0..7) of q = |y| / s,
+// rounded to nearest with ties to the even code: ties at .25, 1.25, 2.5 and 5
+// round down, those at .75, 1.75 and 3.5 round up, above 6 saturates.
+// Instead of forming the quotient, |y| is compared with the products s*T,
+// which are exact in fp32 (s has 4 significant bits, T at most 3). This takes
+// the same decision as rounding the correctly rounded fp32 quotient for every
+// finite |y|: the quotient's rounding can only matter within a couple of ulps
+// of s*T, and an exhaustive sweep there (every scale, every threshold) finds
+// no difference.
+struct E2M1Thresholds {
+  float t[7];
+};
+
+__device__ __forceinline__ E2M1Thresholds e2m1_thresholds(float s) {
+  // s == 0: every magnitude is 0, which +inf thresholds give for finite |y|
+  const float ss = (s != 0.0f) ? s : __builtin_inff();
+  return E2M1Thresholds{{ss * 0.25f, ss * 0.75f, ss * 1.25f, ss * 1.75f, ss * 2.5f, ss * 3.5f,
+                         ss * 5.0f}};
+}
+
+// The magnitude is the number of thresholds |y| passes (strictly for the
+// ties that round down, t[0], t[2], t[4], t[6]); the thresholds ascend, so
+// three comparisons find it: t[3] splits {0..3} from {4..7}, then t[1] or
+// t[5], then one of the strict ones.
+__device__ __forceinline__ uint32_t e2m1_rne(float a, const E2M1Thresholds& th) {
+  const bool b2 = a >= th.t[3];
+  const bool b1 = a >= (b2 ? th.t[5] : th.t[1]);
+  const float tl = b2 ? (b1 ? th.t[6] : th.t[4]) : (b1 ? th.t[2] : th.t[0]);
+  return (b2 ? 4u : 0u) + (b1 ? 2u : 0u) + (a > tl ? 1u : 0u);
 }
 
 // FP4 of the 8 values a lane holds. Lanes (2m, 2m+1) hold one 16-element
@@ -130,11 +152,11 @@ __device__ __forceinline__ void fp4_pair(const float y[8], uint32_t& codes8, uin
   for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(y[e]));
   am = fmaxf(am, __shfl_xor(am, 1));
   const uint32_t sc = e4m3_rne(am / 6.0f);
-  const float s = e4m3_value(sc);
+  const E2M1Thresholds th = e2m1_thresholds(e4m3_value(sc));
   uint32_t c = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const uint32_t mag = (s != 0.0f) ? e2m1_rne(fabsf(y[e]) / s) : 0u;
+    const uint32_t mag = e2m1_rne(fabsf(y[e]), th);
     c |= (((__float_as_uint(y[e]) >> 31) << 3) | mag) << (4 * e);
   }
   codes8 = c;
@@ -150,7 +172,7 @@ __device__ __forceinline__ bool ll_ok(u32x4 w, uint64_t flag) {
 // A word whose flag does not match is re-read with cache-bypassing (volatile)
 // loads, a short sleep apart, at most max_polls times. Returns the last word
 // read; *bad counts a word that never matched.
-__device__ __attribute__((noinline)) u32x4 ll_repoll(const u32x4* p, u32x4 w, uint64_t flag,
+__device__ __forceinline__ u32x4 ll_repoll(const u32x4* p, u32x4 w, uint64_t flag,
                                                      uint32_t max_polls, uint32_t* bad) {
   for (uint32_t i = 0; i < max_polls; ++i) {
     __builtin_amdgcn_s_sleep(2);
@@ -171,46 +193,134 @@ __device__ __forceinline__ u32x4 load16(const u32x4* p) {
 
 __device__ __forceinline__ void store16(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int m = kWave / 2; m > 0; m >>= 1) v += __shfl_xor(v, m);
+// DPP lane move of a double (two 32-bit halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
+// Sum of a double over each row of 16 lanes, in every lane of the row: quad
+// swaps (lane ^ 1, lane ^ 2), then the mirror inside each half row (quad 0
+// with quad 1), then the mirror inside the row (half 0 with half 1). The
+// additions are commutative pairs, so every lane of a row gets the same bits.
+__device__ __forceinline__ double row16_sum(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror
+  v += dpp_f64<0x140>(v);  // row_mirror
   return v;
 }
 
+__device__ __forceinline__ double lane_f64(double v, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                          __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+
+// Sum over the wave's 64 lanes (same value in every lane): the four row sums
+// added in row order. A fixed tree: the result does not depend on timing.
+__device__ __forceinline__ double wave_sum(double v) {
+  v = row16_sum(v);
+  return ((lane_f64(v, 0) + lane_f64(v, 16)) + lane_f64(v, 32)) + lane_f64(v, 48);
+}
+
 // ------------------------------------------------------------- row kernel
+
+// Lane geometry. A thread handles 8 elements of its row per chunk k < VPT, as
+// two groups of 4 (j = 0, 1); group_elem() is the row offset of a group's
+// first element.
+//  plain: the 8 elements are the contiguous 16-byte vector v = k*nthr + lane.
+//  LL: each 16-byte word carries 4 elements, so the wave's 128 words of a
+//      chunk are loaded as two fully contiguous 1 KiB instructions: lane i
+//      takes words i and 64 + i of the wave's tile, i.e. groups at tile
+//      offsets 4i and 256 + 4i.
+template <bool LL>
+__device__ __forceinline__ int64_t group_elem(int k, int j, int lane, int nthr) {
+  if constexpr (LL)
+    return 8 * ((int64_t)k * nthr + (lane & ~(kWave - 1))) + 256 * j + 4 * (lane & (kWave - 1));
+  else
+    return 8 * ((int64_t)k * nthr + lane) + 4 * j;
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x2 load8(const u32x2* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+__device__ __forceinline__ void store8(u32x2* p, u32x2 v) { __builtin_nontemporal_store(v, p); }
+
+// FP4 of a 4-element group in the LL geometry: lanes 4m..4m+3 hold one
+// 16-element block (two XOR shuffles give its max); 4 codes = 16 bits.
+__device__ __forceinline__ void fp4_quad(const float* y, uint32_t& codes4, uint32_t& scale) {
+  float am = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
+  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, __shfl_xor(am, 2));
+  const uint32_t sc = e4m3_rne(am / 6.0f);
+  const E2M1Thresholds th = e2m1_thresholds(e4m3_value(sc));
+  uint32_t c = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    c |= (((__float_as_uint(y[e]) >> 31) << 3) | e2m1_rne(fabsf(y[e]), th)) << (4 * e);
+  codes4 = c;
+  scale = sc;
+}
 
 template <int N, int VPT, bool LL, bool OUT, bool FP4>
 __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   const int lane = threadIdx.x;
   const int nthr = blockDim.x;
-  const int64_t d8 = a.d8;
-  const int64_t row = blockIdx.x;
-  const int64_t base = row * d8;
+  const int64_t d = a.d8 * 8;
+  const int64_t rb = (int64_t)blockIdx.x * d;  // first element of the row
 
-  bool valid[VPT];
-  int64_t vi[VPT];
+  // group offsets, clamped into the row for idle lanes (loads stay in bounds)
+  int64_t eo[VPT][2];
+  bool ok[VPT][2];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    const int64_t v = (int64_t)k * nthr + lane;
-    valid[k] = v < d8;
-    vi[k] = valid[k] ? v : d8 - 1;
+    if constexpr (LL) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t e = group_elem<LL>(k, j, lane, nthr);
+        ok[k][j] = e < d;
+        eo[k][j] = ok[k][j] ? e : d - 4;
+      }
+    } else {  // the two groups of a plain vector share one validity
+      const int64_t e = group_elem<LL>(k, 0, lane, nthr);
+      ok[k][0] = ok[k][1] = e < d;
+      eo[k][0] = ok[k][0] ? e : d - 8;
+      eo[k][1] = eo[k][0] + 4;
+    }
   }
 
   // ---- issue every load of the row
-  constexpr int W = LL ? 2 : 1;  // 16-byte words per 8 elements
-  u32x4 raw[VPT][N][W];
+  u32x4 raw[VPT][N][LL ? 2 : 1];
   u32x4 rres[VPT];
   f32x4 g[VPT][2];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-#pragma unroll
-      for (int w = 0; w < W; ++w) raw[k][i][w] = load16<true>(a.part[i] + (base + vi[k]) * W + w);
+      if constexpr (LL) {
+        raw[k][i][0] = load16<true>(a.part[i] + (rb + eo[k][0]) / 4);
+        raw[k][i][1] = load16<true>(a.part[i] + (rb + eo[k][1]) / 4);
+      } else {
+        raw[k][i][0] = load16<true>(a.part[i] + (rb + eo[k][0]) / 8);
+      }
     }
-    rres[k] = load16<true>(a.residual + base + vi[k]);
-    g[k][0] = a.gamma[2 * vi[k]];
-    g[k][1] = a.gamma[2 * vi[k] + 1];
+    if constexpr (LL) {
+      const u32x2* r2 = (const u32x2*)a.residual;
+      const u32x2 r0 = load8<true>(r2 + (rb + eo[k][0]) / 4);
+      const u32x2 r1 = load8<true>(r2 + (rb + eo[k][1]) / 4);
+      rres[k] = u32x4{r0.x, r0.y, r1.x, r1.y};
+    } else {
+      rres[k] = load16<true>(a.residual + (rb + eo[k][0]) / 8);
+    }
+    g[k][0] = a.gamma[eo[k][0] / 4];
+    g[k][1] = a.gamma[eo[k][1] / 4];
   }
 
   // ---- LL: check flags, re-poll the mismatches, unpack the payload
@@ -221,13 +331,13 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       if constexpr (LL) {
-        u32x4 w0 = raw[k][i][0], w1 = raw[k][i][1];
-        if (valid[k]) {
-          const u32x4* p = a.part[i] + (base + vi[k]) * 2;
-          if (__builtin_expect(!ll_ok(w0, a.ll_flag), 0)) w0 = ll_repoll(p, w0, a.ll_flag, a.max_polls, &bad);
-          if (__builtin_expect(!ll_ok(w1, a.ll_flag), 0)) w1 = ll_repoll(p + 1, w1, a.ll_flag, a.max_polls, &bad);
+        u32x4 w[2] = {raw[k][i][0], raw[k][i][1]};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (ok[k][j] && __builtin_expect(!ll_ok(w[j], a.ll_flag), 0))
+            w[j] = ll_repoll(a.part[i] + (rb + eo[k][j]) / 4, w[j], a.ll_flag, a.max_polls, &bad);
         }
-        pv[k][i] = u32x4{w0.x, w0.y, w1.x, w1.y};
+        pv[k][i] = u32x4{w[0].x, w[0].y, w[1].x, w[1].y};
       } else {
         pv[k][i] = raw[k][i][0];
       }
@@ -250,8 +360,16 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     widen8(rres[k], f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[k][e] = acc[e] + f[e];
-    if (valid[k]) {
-      store16(a.residual_out + base + vi[k], narrow8(h[k]));
+    const u32x4 hb = narrow8(h[k]);
+    if constexpr (LL) {
+      u32x2* ro = (u32x2*)a.residual_out;
+      if (ok[k][0]) store8(ro + (rb + eo[k][0]) / 4, u32x2{hb.x, hb.y});
+      if (ok[k][1]) store8(ro + (rb + eo[k][1]) / 4, u32x2{hb.z, hb.w});
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (ok[k][e / 4]) ss += (double)h[k][e] * (double)h[k][e];
+    } else if (ok[k][0]) {
+      store16(a.residual_out + (rb + eo[k][0]) / 8, hb);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += (double)h[k][e] * (double)h[k][e];
     }
@@ -264,15 +382,16 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     }
   }
 
-  // ---- row reduction: wave XOR tree, then one LDS slot per wave
+  // ---- row reduction: DPP tree inside each wave, one LDS slot per wave, then
+  // every wave sums the (at most 16) slots with the same 16-lane tree
   __shared__ double red[kMaxBlock / kWave];
   ss = wave_sum(ss);
   if ((lane & (kWave - 1)) == 0) red[lane / kWave] = ss;
   __syncthreads();
-  double tot = 0.0;
   const int nw = nthr / kWave;
-  for (int w = 0; w < nw; ++w) tot += red[w];
-  const double inv = 1.0 / sqrt(tot / (double)(d8 * 8) + (double)a.eps);
+  const int wl = lane & (kWave - 1);
+  const double tot = lane_f64(row16_sum(wl < nw ? red[wl] : 0.0), 0);
+  const double inv = 1.0 / sqrt(tot / (double)d + (double)a.eps);
 
   // ---- normalize, scale by gamma, store bf16 and/or FP4
 #pragma unroll
@@ -283,14 +402,35 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = (float)(((double)h[k][e] * inv) * (double)gg[e]);
     if constexpr (OUT) {
-      if (valid[k]) store16(a.out + base + vi[k], narrow8(y));
+      const u32x4 yb = narrow8(y);
+      if constexpr (LL) {
+        u32x2* o2 = (u32x2*)a.out;
+        if (ok[k][0]) store8(o2 + (rb + eo[k][0]) / 4, u32x2{yb.x, yb.y});
+        if (ok[k][1]) store8(o2 + (rb + eo[k][1]) / 4, u32x2{yb.z, yb.w});
+      } else if (ok[k][0]) {
+        store16(a.out + (rb + eo[k][0]) / 8, yb);
+      }
     }
     if constexpr (FP4) {
-      uint32_t c8, sc;
-      fp4_pair(y, c8, sc);
-      if (valid[k]) {
-        __builtin_nontemporal_store(c8, a.codes + base + vi[k]);
-        if ((vi[k] & 1) == 0) a.scales[(base + vi[k]) >> 1] = (uint8_t)sc;
+      if constexpr (LL) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          uint32_t c4, sc;
+          fp4_quad(y + 4 * j, c4, sc);
+          if (ok[k][j]) {
+            const int64_t e = rb + eo[k][j];
+            ((uint16_t*)a.codes)[e / 4] = (uint16_t)c4;
+            if ((lane & 3) == 0) a.scales[e / 16] = (uint8_t)sc;
+          }
+        }
+      } else {
+        uint32_t c8, sc;
+        fp4_pair(y, c8, sc);
+        if (ok[k][0]) {
+          const int64_t e = rb + eo[k][0];
+          __builtin_nontemporal_store(c8, a.codes + e / 8);
+          if ((e & 15) == 0) a.scales[e / 16] = (uint8_t)sc;
+        }
       }
     }
   }
@@ -317,10 +457,16 @@ __global__ __launch_bounds__(256) void quant_kernel(const f32x4* y, int64_t nvec
   }
 }
 
+// The bf16 rounding of the fused kernel applied to an fp32 array (test entry).
+__global__ __launch_bounds__(256) void round_bf16_kernel(const f32x2* x, int64_t npairs,
+                                                         uint32_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < npairs) out[i] = pack_bf16(x[i].x, x[i].y);
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* src, u32x4* dst, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-    store16(dst + i, load16<true>(src + i));
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) store16(dst + i, load16<true>(src + i));
 }
 
 // ------------------------------------------------------------ dispatch
@@ -575,14 +721,31 @@ int arfuse_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) 
   if (bytes > 0 && overlap(range_of(dst, bytes), range_of(src, bytes))) return ARFUSE_ERR_INVALID_ARG;
   if (bytes == 0) return ARFUSE_OK;
   const int64_t n = bytes / 16;
-  int64_t grid = (n + 255) / 256;
-  if (grid > 256 * 32) grid = 256 * 32;  // 32 workgroups per CU, grid-stride beyond
+  const int64_t grid = (n + 255) / 256;  // one 16-byte vector per thread
+  if (grid > 0x7FFFFFFFLL) return ARFUSE_ERR_UNSUPPORTED;
   const u32x4* s = (const u32x4*)src;
   u32x4* dd = (u32x4*)dst;
   int64_t nn = n;
   void* args[] = {&s, &dd, &nn};
   hipError_t e = hipLaunchKernel((const void*)copy_kernel, dim3((unsigned)grid), dim3(256), args, 0,
                                  (hipStream_t)stream);
+  return launch_status(e);
+}
+
+int arfuse_round_bf16(const float* x, int64_t n, uint16_t* out, void* stream) {
+  if (n < 0 || n % 2) return ARFUSE_ERR_INVALID_ARG;
+  if (n == 0) return ARFUSE_OK;
+  if (!x || !out || ((uintptr_t)x & 7u) || ((uintptr_t)out & 3u)) return ARFUSE_ERR_INVALID_ARG;
+  if (overlap(range_of(x, n * 4), range_of(out, n * 2))) return ARFUSE_ERR_INVALID_ARG;
+  const int64_t npairs = n / 2;
+  const int64_t grid = (npairs + 255) / 256;
+  if (grid > 0x7FFFFFFFLL) return ARFUSE_ERR_UNSUPPORTED;
+  const f32x2* xx = (const f32x2*)x;
+  uint32_t* oo = (uint32_t*)out;
+  int64_t np = npairs;
+  void* args[] = {&xx, &np, &oo};
+  hipError_t e = hipLaunchKernel((const void*)round_bf16_kernel, dim3((unsigned)grid), dim3(256),
+                                 args, 0, (hipStream_t)stream);
   return launch_status(e);
 }
 

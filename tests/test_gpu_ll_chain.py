@@ -229,3 +229,21 @@ def test_graph_chain(n, t, d, k, per_call, ll):
         # eager work between replays
         ch.enqueue()
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n,t,d", [(3, 5, 48), (5, 7, 1040), (6, 3, 8208), (2, 2, 65520),
+                                   (8, 9, 4112), (1, 4, 16)])
+def test_ll_ragged_shapes(n, t, d):
+    ci = si.make_call(n, t, d, seed=40 + n + d, outlier_frac=0.2)
+    flag = ci.ll_base + 3
+    words = si.ll_pack_all(ci.partials, flag)
+    ref, bad = oracle_ll(ci, words, flag)
+    assert bad == 0
+    dv = Dev(ci, fp4=True, ll_flag=flag)
+    st = new_status()
+    note("LL ragged n=%d t=%d d=%d" % (n, t, d))
+    got = dv.run(layout=LL, ll_flag=flag, max_polls=1, status=st).fetch()
+    assert read_status(st) == (0, 0)
+    assert_residual_exact(got["residual_out"], ref["residual_out"])
+    assert_y_close(got["out"], ref["y32"], ref["out"])
+    assert_fp4_close(got["codes"], got["scales"], ref["codes"], ref["scales"])

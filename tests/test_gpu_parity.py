@@ -213,3 +213,26 @@ def test_quantize_ragged_rows():
         note("quantize t=%d d=%d" % (t, d))
         c, s = quant_gpu(y)
         assert np.array_equal(s, ws) and np.array_equal(c, wc)
+
+
+def test_kernel_bf16_rounding_on_every_tie_pattern():
+    """The fused kernel's fp32 -> bf16 conversion (gfx950's packed convert)
+    equals the oracle's round-to-nearest-even on every 16-bit prefix combined
+    with each tie and near-tie low half, and on random patterns."""
+    orc = __import__("oracle").default()
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    pats = (hi[:, None] | lows[None, :]).reshape(-1)
+    rnd = np.random.default_rng(14).integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    x = np.concatenate([pats, rnd]).view(np.float32)
+    x = x[np.isfinite(x)]
+    x = x[: x.size // 2 * 2]
+    want = orc.bf16_rne(x)
+    xd = dev_f32(x)
+    out = torch.empty(x.size, dtype=torch.int16, device="cuda:0")
+    note("bf16 rounding sweep n=%d" % x.size)
+    arf.arfuse_round_bf16(xd, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, "bf16 rounding differs at %s" % x[bad[:4]].view(np.uint32)
