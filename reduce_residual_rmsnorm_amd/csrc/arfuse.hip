@@ -269,27 +269,55 @@ __device__ __forceinline__ void fp4_quad(const float* y, uint32_t& codes4, uint3
   scale = sc;
 }
 
+// Typed access at a byte offset from a base pointer. Row base pointers are
+// uniform across the workgroup (scalar registers) and lane offsets fit in 32
+// bits (rows are at most 65536 elements), so every load and store takes the
+// scalar-base + 32-bit vector-offset form and a lane keeps one offset register
+// for all N + 1 input streams instead of a 64-bit address per stream; that
+// leaves room to keep all of a row's loads in flight at once.
+template <typename T>
+__device__ __forceinline__ const T* at(const char* base, uint32_t off) {
+  return reinterpret_cast<const T*>(base + off);
+}
+template <typename T>
+__device__ __forceinline__ T* at_w(char* base, uint32_t off) {
+  return reinterpret_cast<T*>(base + off);
+}
+
 template <int N, int VPT, bool LL, bool OUT, bool FP4>
 __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   const int lane = threadIdx.x;
   const int nthr = blockDim.x;
-  const int64_t d = a.d8 * 8;
+  const uint32_t d = (uint32_t)(a.d8 * 8);
   const int64_t rb = (int64_t)blockIdx.x * d;  // first element of the row
 
-  // group offsets, clamped into the row for idle lanes (loads stay in bounds)
-  int64_t eo[VPT][2];
+  // row bases: partials (bf16, or LL words of 4 bytes per element), residual,
+  // outputs (bf16), FP4 codes (half a byte per element), scales (1/16)
+  const char* prow[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) prow[i] = (const char*)a.part[i] + rb * (LL ? 4 : 2);
+  const char* rrow = (const char*)a.residual + rb * 2;
+  const char* grow = (const char*)a.gamma;
+  char* orow = (char*)a.residual_out + rb * 2;
+  char* yrow = (char*)a.out + rb * 2;
+  char* crow = (char*)a.codes + rb / 2;
+  char* srow = (char*)a.scales + rb / 16;
+
+  // group offsets (elements), clamped into the row for idle lanes so every
+  // load stays in bounds; idle lanes store nothing and add nothing
+  uint32_t eo[VPT][2];
   bool ok[VPT][2];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     if constexpr (LL) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int64_t e = group_elem<LL>(k, j, lane, nthr);
+        const uint32_t e = (uint32_t)group_elem<LL>(k, j, lane, nthr);
         ok[k][j] = e < d;
         eo[k][j] = ok[k][j] ? e : d - 4;
       }
     } else {  // the two groups of a plain vector share one validity
-      const int64_t e = group_elem<LL>(k, 0, lane, nthr);
+      const uint32_t e = (uint32_t)group_elem<LL>(k, 0, lane, nthr);
       ok[k][0] = ok[k][1] = e < d;
       eo[k][0] = ok[k][0] ? e : d - 8;
       eo[k][1] = eo[k][0] + 4;
@@ -305,42 +333,58 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       if constexpr (LL) {
-        raw[k][i][0] = load16<true>(a.part[i] + (rb + eo[k][0]) / 4);
-        raw[k][i][1] = load16<true>(a.part[i] + (rb + eo[k][1]) / 4);
+        raw[k][i][0] = load16<true>(at<u32x4>(prow[i], eo[k][0] * 4));
+        raw[k][i][1] = load16<true>(at<u32x4>(prow[i], eo[k][1] * 4));
       } else {
-        raw[k][i][0] = load16<true>(a.part[i] + (rb + eo[k][0]) / 8);
+        raw[k][i][0] = load16<true>(at<u32x4>(prow[i], eo[k][0] * 2));
       }
     }
     if constexpr (LL) {
-      const u32x2* r2 = (const u32x2*)a.residual;
-      const u32x2 r0 = load8<true>(r2 + (rb + eo[k][0]) / 4);
-      const u32x2 r1 = load8<true>(r2 + (rb + eo[k][1]) / 4);
+      const u32x2 r0 = load8<true>(at<u32x2>(rrow, eo[k][0] * 2));
+      const u32x2 r1 = load8<true>(at<u32x2>(rrow, eo[k][1] * 2));
       rres[k] = u32x4{r0.x, r0.y, r1.x, r1.y};
     } else {
-      rres[k] = load16<true>(a.residual + (rb + eo[k][0]) / 8);
+      rres[k] = load16<true>(at<u32x4>(rrow, eo[k][0] * 2));
     }
-    g[k][0] = a.gamma[eo[k][0] / 4];
-    g[k][1] = a.gamma[eo[k][1] / 4];
+    g[k][0] = *at<f32x4>(grow, eo[k][0] * 4);
+    g[k][1] = *at<f32x4>(grow, eo[k][1] * 4);
   }
+  // keep the scheduler from interleaving arithmetic into the load block: all
+  // N + 3 loads of the row are in flight before the first use
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- LL: check flags, re-poll the mismatches, unpack the payload
+  // ---- LL: check every flag with plain compares; only a lane holding a
+  // mismatched word takes the (bounded) re-poll path. Then unpack the payload.
   uint32_t bad = 0;
   u32x4 pv[VPT][N];
+  if constexpr (LL) {
+    bool all_ok = true;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) all_ok &= !ok[k][j] || ll_ok(raw[k][i][j], a.ll_flag);
+    if (__builtin_expect(!all_ok, 0)) {
+#pragma unroll
+      for (int k = 0; k < VPT; ++k)
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            if (ok[k][j] && !ll_ok(raw[k][i][j], a.ll_flag))
+              raw[k][i][j] = ll_repoll(at<u32x4>(prow[i], eo[k][j] * 4), raw[k][i][j], a.ll_flag,
+                                       a.max_polls, &bad);
+    }
+  }
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      if constexpr (LL) {
-        u32x4 w[2] = {raw[k][i][0], raw[k][i][1]};
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (ok[k][j] && __builtin_expect(!ll_ok(w[j], a.ll_flag), 0))
-            w[j] = ll_repoll(a.part[i] + (rb + eo[k][j]) / 4, w[j], a.ll_flag, a.max_polls, &bad);
-        }
-        pv[k][i] = u32x4{w[0].x, w[0].y, w[1].x, w[1].y};
-      } else {
+      if constexpr (LL)
+        pv[k][i] = u32x4{raw[k][i][0].x, raw[k][i][0].y, raw[k][i][1].x, raw[k][i][1].y};
+      else
         pv[k][i] = raw[k][i][0];
-      }
     }
   }
 
@@ -362,14 +406,13 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     for (int e = 0; e < 8; ++e) h[k][e] = acc[e] + f[e];
     const u32x4 hb = narrow8(h[k]);
     if constexpr (LL) {
-      u32x2* ro = (u32x2*)a.residual_out;
-      if (ok[k][0]) store8(ro + (rb + eo[k][0]) / 4, u32x2{hb.x, hb.y});
-      if (ok[k][1]) store8(ro + (rb + eo[k][1]) / 4, u32x2{hb.z, hb.w});
+      if (ok[k][0]) store8(at_w<u32x2>(orow, eo[k][0] * 2), u32x2{hb.x, hb.y});
+      if (ok[k][1]) store8(at_w<u32x2>(orow, eo[k][1] * 2), u32x2{hb.z, hb.w});
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (ok[k][e / 4]) ss += (double)h[k][e] * (double)h[k][e];
     } else if (ok[k][0]) {
-      store16(a.residual_out + (rb + eo[k][0]) / 8, hb);
+      store16(at_w<u32x4>(orow, eo[k][0] * 2), hb);
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += (double)h[k][e] * (double)h[k][e];
     }
@@ -404,11 +447,10 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     if constexpr (OUT) {
       const u32x4 yb = narrow8(y);
       if constexpr (LL) {
-        u32x2* o2 = (u32x2*)a.out;
-        if (ok[k][0]) store8(o2 + (rb + eo[k][0]) / 4, u32x2{yb.x, yb.y});
-        if (ok[k][1]) store8(o2 + (rb + eo[k][1]) / 4, u32x2{yb.z, yb.w});
+        if (ok[k][0]) store8(at_w<u32x2>(yrow, eo[k][0] * 2), u32x2{yb.x, yb.y});
+        if (ok[k][1]) store8(at_w<u32x2>(yrow, eo[k][1] * 2), u32x2{yb.z, yb.w});
       } else if (ok[k][0]) {
-        store16(a.out + (rb + eo[k][0]) / 8, yb);
+        store16(at_w<u32x4>(yrow, eo[k][0] * 2), yb);
       }
     }
     if constexpr (FP4) {
@@ -418,18 +460,16 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
           uint32_t c4, sc;
           fp4_quad(y + 4 * j, c4, sc);
           if (ok[k][j]) {
-            const int64_t e = rb + eo[k][j];
-            ((uint16_t*)a.codes)[e / 4] = (uint16_t)c4;
-            if ((lane & 3) == 0) a.scales[e / 16] = (uint8_t)sc;
+            *at_w<uint16_t>(crow, eo[k][j] / 2) = (uint16_t)c4;
+            if ((lane & 3) == 0) *at_w<uint8_t>(srow, eo[k][j] / 16) = (uint8_t)sc;
           }
         }
       } else {
         uint32_t c8, sc;
         fp4_pair(y, c8, sc);
         if (ok[k][0]) {
-          const int64_t e = rb + eo[k][0];
-          __builtin_nontemporal_store(c8, a.codes + e / 8);
-          if ((e & 15) == 0) a.scales[e / 16] = (uint8_t)sc;
+          __builtin_nontemporal_store(c8, at_w<uint32_t>(crow, eo[k][0] / 2));
+          if ((eo[k][0] & 15) == 0) *at_w<uint8_t>(srow, eo[k][0] / 16) = (uint8_t)sc;
         }
       }
     }
