@@ -71,6 +71,11 @@ def _declare(lib):
     lib.oracle_rmsnorm_rows.restype = c.c_int
     lib.oracle_ll_unpack.argtypes = [P, I64, c.c_uint64, P]
     lib.oracle_ll_unpack.restype = c.c_int64
+    lib.oracle_quantize_fp8.argtypes = [P, I64, I64, c.c_float, P]
+    lib.oracle_fused.argtypes = [P, c.c_int, P, P, c.c_float, I64, I64, P, P, P, P, P, P, c.c_float]
+    lib.oracle_fused.restype = c.c_int
+    lib.oracle_sentinel_pending.argtypes = [P, I64, c.c_uint16]
+    lib.oracle_sentinel_pending.restype = c.c_int64
     return lib
 
 
@@ -176,6 +181,46 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_allreduce_rmsnorm rejected its arguments")
         return dict(residual_out=r_out, y32=y32, out=out, codes=codes, scales=scales)
+
+    def quantize_fp8(self, y, inv_scale):
+        y = _c(y, np.float32)
+        out = np.empty(y.shape, np.uint8)
+        t, d = y.shape
+        self.lib.oracle_quantize_fp8(_ptr(y), t, d, float(inv_scale), _ptr(out))
+        return out
+
+    def fused(self, partials, residual, gamma, eps, t=None, d=None, out=True, fp4=False,
+              fp8_inv_scale=None, residual_out=True):
+        """Any pattern: residual and/or gamma may be None. Returns a dict."""
+        parts = [_c(p, np.uint16) for p in partials]
+        t, d = parts[0].shape if t is None else (t, d)
+        res = _c(residual, np.uint16) if residual is not None else None
+        g = _c(gamma, np.float32) if gamma is not None else None
+        arr = (ctypes.c_void_p * len(parts))(*[p.ctypes.data for p in parts])
+        nul = ctypes.c_void_p(0)
+        norm = g is not None
+        r = dict(residual_out=np.empty((t, d), np.uint16) if residual_out else None,
+                 y32=np.empty((t, d), np.float32) if norm else None,
+                 out=np.empty((t, d), np.uint16) if (norm and out) else None,
+                 codes=np.empty((t, d // 2), np.uint8) if (norm and fp4) else None,
+                 scales=np.empty((t, d // 16), np.uint8) if (norm and fp4) else None,
+                 fp8=np.empty((t, d), np.uint8) if (norm and fp8_inv_scale is not None) else None)
+        pp = {k: (_ptr(v) if v is not None else nul) for k, v in r.items()}
+        rc = self.lib.oracle_fused(arr, len(parts), _ptr(res) if res is not None else nul,
+                                   _ptr(g) if g is not None else nul, float(eps), t, d,
+                                   pp["residual_out"], pp["y32"], pp["out"], pp["codes"],
+                                   pp["scales"], pp["fp8"],
+                                   float(fp8_inv_scale if fp8_inv_scale is not None else 1.0))
+        if rc != 0:
+            raise ValueError("oracle_fused rejected its arguments")
+        return r
+
+    def sentinel_pending(self, part, sentinel: int) -> int:
+        p = _c(part, np.uint16)
+        n = self.lib.oracle_sentinel_pending(_ptr(p), p.size, int(sentinel))
+        if n < 0:
+            raise ValueError("oracle_sentinel_pending rejected its arguments")
+        return int(n)
 
     def ll_unpack(self, words, n_elems: int, flag: int):
         w = _c(words, np.uint8)

@@ -185,6 +185,17 @@ void oracle_quantize_fp4(const float* y, int64_t t, int64_t d, uint8_t* codes,
   }
 }
 
+/* ------------------------------------------------------------ FP8 output */
+
+/* Per-tensor FP8: q = fl32(y * inv_scale) (one IEEE multiply), then the
+ * nearest E4M3 magnitude (saturating at 448) with y's sign bit. */
+void oracle_quantize_fp8(const float* y, int64_t t, int64_t d, float inv_scale, uint8_t* out) {
+  for (int64_t e = 0; e < t * d; ++e) {
+    float q = y[e] * inv_scale;
+    out[e] = (uint8_t)((signbit(q) ? 0x80u : 0u) | oracle_e4m3_rne(fabsf(q)));
+  }
+}
+
 /* ------------------------------------------------- sum, residual, RMSNorm */
 
 /* acc = f32(p_0); acc = acc ⊕ f32(p_i) for i = 1..N-1; h = acc ⊕ f32(res).
@@ -224,7 +235,20 @@ int oracle_allreduce_rmsnorm(const uint16_t* const* partials, int n,
                              float eps, int64_t t, int64_t d,
                              uint16_t* residual_out, float* y32, uint16_t* out,
                              uint8_t* codes, uint8_t* scales) {
-  if (n < 1 || t < 0 || d <= 0 || !partials || !residual || !gamma) return -1;
+  if (!residual || !gamma) return -1;
+  return oracle_fused(partials, n, residual, gamma, eps, t, d, residual_out, y32, out, codes,
+                      scales, NULL, 1.0f);
+}
+
+/* Every pattern of the fused operator (Deep Dive §6.3, pattern table): with
+ * a residual, h = sum + residual, else h = sum; with gamma, RMSNorm and the
+ * requested outputs, else only residual_out = bf16(h) (the all-reduce). */
+int oracle_fused(const uint16_t* const* partials, int n, const uint16_t* residual,
+                 const float* gamma, float eps, int64_t t, int64_t d,
+                 uint16_t* residual_out, float* y32, uint16_t* out, uint8_t* codes,
+                 uint8_t* scales, uint8_t* fp8_out, float fp8_inv_scale) {
+  if (n < 1 || t < 0 || d <= 0 || !partials) return -1;
+  if (!gamma && (y32 || out || codes || fp8_out)) return -1;
   if ((codes == NULL) != (scales == NULL)) return -1;
   if (codes && d % 16) return -1;
   for (int i = 0; i < n; ++i)
@@ -242,19 +266,42 @@ int oracle_allreduce_rmsnorm(const uint16_t* const* partials, int n,
     /* one row at a time keeps the working set small; the arithmetic is the
      * same element-wise definition as oracle_rank_sum_residual */
     for (int i = 0; i < n; ++i) prow[i] = partials[i] + r * d;
-    oracle_rank_sum_residual(prow, n, residual + r * d, 1, d, h);
+    if (residual) {
+      oracle_rank_sum_residual(prow, n, residual + r * d, 1, d, h);
+    } else {
+      for (int64_t j = 0; j < d; ++j) {
+        float acc = oracle_bf16_to_f32(prow[0][j]);
+        for (int i = 1; i < n; ++i) acc = acc + oracle_bf16_to_f32(prow[i][j]);
+        h[j] = acc;
+      }
+    }
     if (residual_out)
       for (int64_t j = 0; j < d; ++j) residual_out[r * d + j] = oracle_bf16_rne(h[j]);
+    if (!gamma) continue;
     oracle_rmsnorm_rows(h, gamma, eps, 1, d, y);
     if (y32) memcpy(y32 + r * d, y, sizeof(float) * (size_t)d);
     if (out)
       for (int64_t j = 0; j < d; ++j) out[r * d + j] = oracle_bf16_rne(y[j]);
     if (codes) oracle_quantize_fp4(y, 1, d, codes + r * (d / 2), scales + r * (d / 16));
+    if (fp8_out) oracle_quantize_fp8(y, 1, d, fp8_inv_scale, fp8_out + r * d);
   }
   free(h);
   free(y);
   free(prow);
   return 0;
+}
+
+/* ------------------------------------------------------------ sentinel */
+
+int64_t oracle_sentinel_pending(const uint16_t* part, int64_t n_elems, uint16_t sentinel) {
+  if (!part || n_elems < 0 || n_elems % 8) return -1;
+  int64_t pending = 0;
+  for (int64_t v = 0; v < n_elems / 8; ++v) {
+    int hit = 0;
+    for (int k = 0; k < 8; ++k) hit |= part[8 * v + k] == sentinel;
+    pending += hit;
+  }
+  return pending;
 }
 
 /* ----------------------------------------------------------------- LL words */

@@ -68,6 +68,25 @@ int oracle_rank_sum_residual(const uint16_t* const* partials, int n,
 int oracle_rmsnorm_rows(const float* h, const float* gamma, float eps,
                         int64_t t, int64_t d, float* y32);
 
+/* FP8 E4M3 of fp32 y [t][d] with a per-tensor reciprocal scale:
+ * code = sign(y) << 7 | E4M3(|fl32(y * inv_scale)|), magnitudes above 448
+ * giving 448. out: uint8 [t][d]. */
+void oracle_quantize_fp8(const float* y, int64_t t, int64_t d, float inv_scale, uint8_t* out);
+
+/* The fused call with every pattern: residual may be NULL (no residual add);
+ * gamma may be NULL (no RMSNorm: only residual_out = bf16(h) is produced).
+ * fp8_out (uint8 [t][d], may be NULL) quantizes y32 with inv_scale.
+ * Returns 0, or -1 on a bad argument. */
+int oracle_fused(const uint16_t* const* partials, int n, const uint16_t* residual,
+                 const float* gamma, float eps, int64_t t, int64_t d,
+                 uint16_t* residual_out, float* y32, uint16_t* out, uint8_t* codes,
+                 uint8_t* scales, uint8_t* fp8_out, float fp8_inv_scale);
+
+/* Sentinel-mode arrival check of one partial: the number of 16-byte vectors
+ * (8 consecutive bf16 elements, n_elems % 8 == 0) holding the 16-bit sentinel
+ * pattern in at least one element, i.e. not yet fully written. */
+int64_t oracle_sentinel_pending(const uint16_t* part, int64_t n_elems, uint16_t sentinel);
+
 /* LL decode of one partial: words is uint8 [n_elems/4][16] (4 bf16 payload
  * elements then a uint64 flag per 16-byte word). Writes the payload to out
  * (bf16 [n_elems]) and returns how many words carry a flag other than

@@ -438,10 +438,85 @@ def pin_ll_roundtrip(orc):
     assert bad == p.size // 4
 
 
+# ------------------------------------------------------------- FP8 pins
+
+def pin_fp8_exact(orc):
+    """FP8 output: code = sign | E4M3(|fl32(y * inv_scale)|), checked by
+    exact-rational nearest-even around every E4M3 tie (both signs), against
+    PyTorch's float8_e4m3fn below 464, and saturating to 448 above."""
+    pts = _e4m3_sweep_points()
+    y = np.concatenate([pts, -pts, np.array([-0.0, 0.0, 1e6, -1e6, 500.0], np.float32)])
+    y = y.astype(np.float32).reshape(1, -1)
+    got = orc.quantize_fp8(y, np.float32(1.0))[0]
+    for v, c in zip(y[0], got):
+        mag = 0x7E if abs(float(v)) > 448 else nearest_even(abs(Fr(float(v))), E4M3)
+        want = (0x80 if math.copysign(1.0, float(v)) < 0 else 0) | mag
+        assert c == want, "fp8 of %r: 0x%02x vs 0x%02x" % (float(v), c, want)
+    ok = np.abs(y[0]) < 464
+    tref = torch.from_numpy(y[0][ok].copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got[ok], tref)
+    # the scale is one fp32 multiply before rounding
+    rng = np.random.default_rng(15)
+    y = rng.standard_normal((4, 64)).astype(np.float32) * np.float32(3)
+    inv = np.float32(37.5)
+    got = orc.quantize_fp8(y, inv)
+    want = orc.quantize_fp8((y * inv).astype(np.float32), np.float32(1.0))
+    assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------ pattern pins
+
+def pin_patterns(orc):
+    """Without a residual the fused call normalizes the rank sum itself
+    (rank-order probe, summation bound, rms_norm of the sum); without gamma
+    it is the plain all-reduce: residual_out = bf16 of the rank-ordered sum,
+    and the residual, when given, added last."""
+    P = [_bf16([[2.0 ** 24]]), _bf16([[1.0]]), _bf16([[-(2.0 ** 24)]])]
+    r = orc.fused(P, None, None, 0.0)
+    assert r["residual_out"][0, 0] == 0
+    r = orc.fused(P[:2], _bf16([[-(2.0 ** 24)]]), None, 0.0)
+    assert r["residual_out"][0, 0] == 0
+    z = _bf16([[-0.0]])
+    r = orc.fused([z, z, z], None, None, 0.0)
+    assert r["residual_out"][0, 0] == 0x8000, "the sum starts from p0: -0 + -0 + -0 is -0"
+    ci = si.make_call(4, 3, 256, seed=16)
+    r = orc.fused(ci.partials, None, ci.gamma, ci.eps)
+    zero = np.zeros_like(ci.residual)
+    h = orc.rank_sum_residual(ci.partials, zero)     # + 0.0 changes nothing here
+    assert np.array_equal(r["residual_out"], si.to_bf16_bits(h))
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(h).double(), (256,),
+                                       weight=torch.from_numpy(ci.gamma).double(),
+                                       eps=float(ci.eps)).float().numpy()
+    ulps = np.abs(r["y32"].view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1
+    full = orc.allreduce_rmsnorm(ci.partials, ci.residual, ci.gamma, ci.eps, fp4=True)
+    r = orc.fused(ci.partials, ci.residual, None, ci.eps)
+    assert np.array_equal(r["residual_out"], full["residual_out"]) and r["y32"] is None
+    r = orc.fused(ci.partials, ci.residual, ci.gamma, ci.eps, fp4=True, fp8_inv_scale=2.0)
+    assert np.array_equal(r["codes"], full["codes"]) and np.array_equal(r["y32"], full["y32"])
+    assert np.array_equal(r["fp8"], orc.quantize_fp8(full["y32"], np.float32(2.0)))
+
+
+# ----------------------------------------------------------- sentinel pins
+
+def pin_sentinel_pending(orc):
+    """A 16-byte vector (8 elements) is pending while any of its elements
+    still holds the sentinel pattern; brute force on small arrays."""
+    rng = np.random.default_rng(17)
+    for sentinel in (0xFFFF, 0x8000):
+        for _ in range(20):
+            a = si.to_bf16_bits(rng.standard_normal(64).astype(np.float32))
+            a[a == sentinel] = 0
+            hits = rng.choice(64, size=int(rng.integers(0, 12)), replace=False)
+            a[hits] = sentinel
+            want = len({int(h) // 8 for h in hits})
+            assert orc.sentinel_pending(a, sentinel) == want
+
+
 ALL_PINS = [
     pin_bf16_vs_torch, pin_e4m3_decode_vs_torch, pin_e4m3_rne_exact, pin_e2m1_rne_exact,
     pin_fp4_code_ties, pin_fp4_scale_ties, pin_fp4_small_random_blocks, pin_fp4_invariants,
     pin_rank_order, pin_summation_bound, pin_residual_out_is_bf16_of_h,
     pin_rmsnorm_vs_torch_f64, pin_fused_uses_fp32_h, pin_closed_forms, pin_scale_invariance,
-    pin_ll_roundtrip,
+    pin_ll_roundtrip, pin_fp8_exact, pin_patterns, pin_sentinel_pending,
 ]

@@ -65,6 +65,13 @@ MUTANTS = {
     "sign_of_zero_lost": [("(signbit(y[j]) ? 8u : 0u)", "(y[j] < 0.0f ? 8u : 0u)")],
     "block_max_signed": [("float a = fabsf(y[j]);", "float a = y[j];")],
     "zero_scale_not_special": [("if (s != 0.0f) mag = oracle_e2m1_rne", "mag = oracle_e2m1_rne")],
+    "fp8_sign_dropped": [("out[e] = (uint8_t)((signbit(q) ? 0x80u : 0u) | oracle_e4m3_rne(fabsf(q)));",
+                          "out[e] = (uint8_t)oracle_e4m3_rne(fabsf(q));")],
+    "fp8_scale_divides": [("float q = y[e] * inv_scale;", "float q = y[e] / inv_scale;")],
+    "no_residual_adds_zero_first": [
+        ("        float acc = oracle_bf16_to_f32(prow[0][j]);\n        for (int i = 1; i < n; ++i)",
+         "        float acc = 0.0f + oracle_bf16_to_f32(prow[0][j]);\n        for (int i = 1; i < n; ++i)")],
+    "sentinel_counted_per_element": [("    pending += hit;", "    for (int k = 0; k < 8; ++k) pending += part[8 * v + k] == sentinel;")],
     "ll_flag_misread": [("flag = (flag << 8) | p[8 + k];", "flag = (flag << 8) | p[7 + k];")],
     "ll_payload_bytes_swapped": [
         ("(uint16_t)(p[2 * k] | ((uint16_t)p[2 * k + 1] << 8))",
