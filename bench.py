@@ -38,7 +38,9 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published peak
 INFINITY_CACHE_BYTES = 256 << 20
 METRIC = "fused kernel HBM GB/s (% of peak) at prefill; µs/call p50 at decode shapes"
-KERNEL_SRC = os.path.join(ROOT, "reduce_residual_rmsnorm_amd", "csrc", "arfuse.hip")
+_CSRC = os.path.join(ROOT, "reduce_residual_rmsnorm_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("arfuse_device.hpp", "arfuse_rows.hip",
+                                                    "arfuse.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -55,13 +57,20 @@ def plane_bytes(t: int, d: int) -> int:
 
 
 def algorithmic_bytes(n: int, t: int, d: int, ll: bool = False, out: bool = True,
-                      fp4: bool = False):
+                      fp4: bool = False, residual: bool = True, norm: bool = True,
+                      rout: bool = True, fp8: bool = False, reset: bool = False):
     """(read, write) bytes one fused call must move: N partials (twice the
     bytes when LL-packed), the residual and gamma (fp32) read; residual_out,
-    and y (bf16) and/or FP4 codes + scales written."""
+    and y (bf16) and/or FP4 codes + scales and/or FP8 codes written, plus the
+    N slot planes refilled with the sentinel when the call resets a set.
+    Without gamma (all-reduce only) nothing past residual_out is read or
+    written."""
     P = plane_bytes(t, d)
-    reads = n * P * (2 if ll else 1) + P + 4 * d
-    writes = P + (P if out else 0) + ((t * d // 2 + t * d // 16) if fp4 else 0)
+    reads = n * P * (2 if ll else 1) + (P if residual else 0) + (4 * d if norm else 0)
+    writes = (P if rout else 0) + (n * P if reset else 0)
+    if norm:
+        writes += (P if out else 0) + ((t * d // 2 + t * d // 16) if fp4 else 0)
+        writes += t * d if fp8 else 0
     return reads, writes
 
 
@@ -85,8 +94,12 @@ def page_unfused_bytes_per_token(d: int):
 
 
 def source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of every device source the row kernel is built from."""
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # ------------------------------------------------------------ device helpers
@@ -110,28 +123,43 @@ def dev_bytes(a):
 
 class PrefillSets:
     """`nsets` device copies of one call's inputs plus outputs, rotated so
-    consecutive calls touch disjoint memory."""
+    consecutive calls touch disjoint memory. The keyword arguments select a
+    fusion pattern (see `algorithmic_bytes`); `reset` runs the sentinel
+    layout and refills a separate slot set of N planes on every call."""
 
-    def __init__(self, ci, nsets: int, fp4: bool = False, out: bool = True):
+    def __init__(self, ci, nsets: int, fp4: bool = False, out: bool = True,
+                 residual: bool = True, norm: bool = True, rout: bool = True,
+                 fp8: bool = False, reset: bool = False):
         import torch
         self.ci = ci
         self.sets = []
+        self.reset = reset
+        self.plain = residual and norm and rout and not fp8 and not reset
         parts0 = [dev_bf16(p) for p in ci.partials]
         res0 = dev_bf16(ci.residual)
-        gamma = torch.from_numpy(ci.gamma).to(_dev())
+        gamma = torch.from_numpy(ci.gamma).to(_dev()) if norm else None
+        t, d = ci.t, ci.d
         for s in range(nsets):
             parts = parts0 if s == 0 else [p.clone() for p in parts0]
-            res = res0 if s == 0 else res0.clone()
-            o = torch.empty_like(res0) if out else None
-            ro = torch.empty_like(res0)
-            codes = torch.empty((ci.t, ci.d // 2), dtype=torch.uint8, device=_dev()) if fp4 else None
-            scales = torch.empty((ci.t, ci.d // 16), dtype=torch.uint8, device=_dev()) if fp4 else None
-            self.sets.append((parts, res, gamma, o, ro, codes, scales))
+            res = (res0 if s == 0 else res0.clone()) if residual else None
+            o = torch.empty_like(res0) if (out and norm) else None
+            ro = torch.empty_like(res0) if rout else None
+            codes = torch.empty((t, d // 2), dtype=torch.uint8, device=_dev()) if fp4 else None
+            scales = torch.empty((t, d // 16), dtype=torch.uint8, device=_dev()) if fp4 else None
+            f8 = torch.empty((t, d), dtype=torch.uint8, device=_dev()) if fp8 else None
+            slots = [torch.empty_like(res0) for _ in parts] if reset else None
+            self.sets.append((parts, res, gamma, o, ro, codes, scales, f8, slots))
 
     def call(self, i: int):
         import reduce_residual_rmsnorm_amd as arf
-        parts, res, gamma, o, ro, codes, scales = self.sets[i % len(self.sets)]
-        arf.arfuse_rmsnorm(parts, res, gamma, float(self.ci.eps), o, ro, codes, scales)
+        parts, res, gamma, o, ro, codes, scales, f8, slots = self.sets[i % len(self.sets)]
+        if self.plain:
+            arf.arfuse_rmsnorm(parts, res, gamma, float(self.ci.eps), o, ro, codes, scales)
+            return
+        arf.arfuse_rmsnorm_ex(parts, res, gamma, float(self.ci.eps), o, ro, codes, scales,
+                              t=self.ci.t, d=self.ci.d,
+                              layout=arf.ARFUSE_LAYOUT_SENTINEL if self.reset else 0,
+                              reset=slots, fp8_out=f8, fp8_inv_scale=4.0)
 
 
 def n_sets_for(call_bytes: int) -> int:
@@ -178,10 +206,13 @@ def time_graph(g, reps: int):
 # ------------------------------------------------------------ decode chains
 
 def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = False,
-                 out: bool = True, reps: int = 200, seed: int = 0):
+                 out: bool = True, reps: int = 200, seed: int = 0, fp8: bool = False,
+                 sentinel: bool = False):
     """µs per call of a k-call chain captured in one graph (call c reads call
     c-1's residual_out), and of the same-length graph of the empty kernel
-    with the same launch (the per-node floor)."""
+    with the same launch (the per-node floor). `sentinel` reads the slots in
+    the sentinel layout and refills a second slot set on every call (the
+    triple-buffer reset), `fp8` adds the FP8 output."""
     import numpy as np
     import torch
 
@@ -205,7 +236,10 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
     codes = torch.empty((t, d // 2), dtype=torch.uint8, device=_dev()) if fp4 else None
     scales = torch.empty((t, d // 16), dtype=torch.uint8, device=_dev()) if fp4 else None
     status = torch.zeros(4, dtype=torch.int32, device=_dev())
-    epi = (arf.ARFUSE_EPI_BF16 if out else 0) | (arf.ARFUSE_EPI_FP4 if fp4 else 0)
+    f8 = torch.empty((t, d), dtype=torch.uint8, device=_dev()) if fp8 else None
+    slots = [torch.empty_like(res0) for _ in range(n)] if sentinel else None
+    epi = ((arf.ARFUSE_EPI_BF16 if out else 0) | (arf.ARFUSE_EPI_FP4 if fp4 else 0)
+           | (arf.ARFUSE_EPI_FP8 if fp8 else 0))
 
     def enqueue():
         for c in range(k):
@@ -215,12 +249,19 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
                 arf.arfuse_rmsnorm_ex(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales,
                                       layout=arf.ARFUSE_LAYOUT_LL, ll_flag=flags[c], max_polls=4,
                                       status=status)
+            elif sentinel or fp8:
+                arf.arfuse_rmsnorm_ex(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales,
+                                      layout=arf.ARFUSE_LAYOUT_SENTINEL if sentinel else 0,
+                                      max_polls=4, status=status, reset=slots, fp8_out=f8,
+                                      fp8_inv_scale=4.0)
             else:
                 arf.arfuse_rmsnorm(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales)
 
     def enqueue_floor():
+        lay = (arf.ARFUSE_LAYOUT_LL if ll else
+               arf.ARFUSE_LAYOUT_SENTINEL if sentinel else arf.ARFUSE_LAYOUT_PLAIN)
         for _ in range(k):
-            arf.arfuse_launch_floor(n, t, d, epi, layout=arf.ARFUSE_LAYOUT_LL if ll else 0)
+            arf.arfuse_launch_floor(n, t, d, epi, layout=lay)
 
     enqueue()
     torch.cuda.synchronize()
@@ -233,10 +274,11 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
     chain = time_graph(g, reps)
     floor = time_graph(gf, reps)
     st = status.cpu().numpy().view(np.uint32)
-    if ll and st[0] != 0:
-        raise RuntimeError("LL flags reported bad during the benchmark: %s" % st)
+    if st[0] != 0:
+        raise RuntimeError("arrival reported bad during the benchmark: %s" % st)
     info = arf.arfuse_query_launch(n, t, d, epi)
-    r = dict(n=n, t=t, d=d, calls=k, layout="ll" if ll else "plain", fp4=fp4,
+    r = dict(n=n, t=t, d=d, calls=k, layout="ll" if ll else "sentinel" if sentinel else "plain",
+             fp4=fp4, fp8=fp8, reset=sentinel,
              grid=int(info.grid), block=int(info.block),
              us_per_call_p50=chain["p50"] / k, chain_us_p50=chain["p50"],
              chain_us_p10=chain["p10"], chain_us_p90=chain["p90"],
@@ -246,15 +288,19 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
     return r
 
 
-def prefill_gbps(n: int, t: int, d: int, steps: int, warmup: int, fp4=False, out=True, seed=0):
+def prefill_gbps(n: int, t: int, d: int, steps: int, warmup: int, fp4=False, out=True, seed=0,
+                 **pattern):
+    """Throughput of one fused call shape with rotating buffer sets. `pattern`
+    takes the keyword arguments of `algorithmic_bytes` beyond the shape."""
     import seeded_inputs as si
     ci = si.make_call(n, t, d, seed=seed, outlier_frac=0.001)
-    rd, wr = algorithmic_bytes(n, t, d, out=out, fp4=fp4)
-    sets = PrefillSets(ci, n_sets_for(rd + wr), fp4=fp4, out=out)
+    rd, wr = algorithmic_bytes(n, t, d, out=out, fp4=fp4, **pattern)
+    sets = PrefillSets(ci, n_sets_for(rd + wr), fp4=fp4, out=out, **pattern)
     ms = time_calls(sets.call, steps, warmup)
     r = dict(n=n, t=t, d=d, fp4=fp4, out=out, nsets=len(sets.sets), us_per_call=ms * 1e3,
-             algorithmic_gbps=(rd + wr) / (ms * 1e-3) / 1e9)
-    if not fp4:
+             read_bytes=rd, write_bytes=wr, algorithmic_gbps=(rd + wr) / (ms * 1e-3) / 1e9,
+             **pattern)
+    if not fp4 and not pattern:
         r["counted_gbps"] = counted_bytes(n, t, d) / (ms * 1e-3) / 1e9
     del sets
     return r
@@ -463,6 +509,13 @@ def main(argv=None):
         extras["prefill_n8_t512_d8192"] = prefill_gbps(8, 512, 8192, 100, 10)
         log("fp4 t=512")
         extras["fp4_n4_t512_d8192"] = prefill_gbps(4, 512, 8192, 100, 10, fp4=True, out=False)
+        for label, out_, kw in [("allreduce_only_n8_t4096_d8192", True, dict(norm=False)),
+                                ("fp8_n8_t4096_d8192", False, dict(fp8=True)),
+                                ("no_residual_n8_t4096_d8192", True, dict(residual=False)),
+                                ("sentinel_reset_n8_t4096_d8192", True, dict(reset=True))]:
+            log("pattern %s" % label)
+            extras[label] = prefill_gbps(8, 4096, 8192, 30, 5, out=out_, **kw)
+            torch.cuda.empty_cache()
         for (nn, tt, dd, kk, ll, fp4, label) in [
                 (2, 1, 4096, 100, False, False, "decode_n2_t1_d4096_x100"),
                 (8, 8, 4096, 64, False, False, "decode_n8_t8_d4096_chain64"),
@@ -470,11 +523,14 @@ def main(argv=None):
                 (8, 8, 8192, 160, False, False, "decode_n8_t8_d8192_chain160"),
                 (4, 8, 8192, 160, True, False, "decode_n4_t8_d8192_chain160_ll"),
                 (8, 8, 8192, 160, True, False, "decode_n8_t8_d8192_chain160_ll"),
+                (8, 8, 8192, 160, "sentinel", False, "decode_n8_t8_d8192_chain160_sentinel"),
+                (8, 8, 8192, 160, "fp8", False, "decode_n8_t8_d8192_chain160_fp8"),
                 (4, 1, 8192, 100, False, True, "fp4_n4_t1_d8192_x100"),
                 (4, 8, 8192, 100, False, True, "fp4_n4_t8_d8192_x100"),
                 (4, 64, 8192, 100, False, True, "fp4_n4_t64_d8192_x100")]:
             log("decode %s" % label)
-            extras[label] = decode_chain(nn, tt, dd, kk, ll=ll, fp4=fp4, out=not fp4)
+            extras[label] = decode_chain(nn, tt, dd, kk, ll=ll is True, fp4=fp4, out=not fp4,
+                                         sentinel=ll == "sentinel", fp8=ll == "fp8")
             torch.cuda.empty_cache()
 
     cpu = None

@@ -12,6 +12,12 @@
  *   out       = bf16(y)                         optional
  *   FP4       = per 16 consecutive elements of y: scale s = E4M3(max|y| / 6),
  *               code = sign | E2M1(|y| / s)     optional
+ *   FP8       = sign | E4M3(|y * inv_scale|)    optional (arfuse_rmsnorm_ex)
+ *
+ * The fusion patterns of the pages' fused operator are selected by which
+ * pointers are given: no residual (h = the rank sum), and no gamma (no
+ * RMSNorm: residual_out = bf16(sum [+ residual]) is then the plain all-reduce
+ * result and the only output).
  *
  * Where the pages define it:
  *  - The all-reduce of tensor parallelism sums same-shaped partial products of
@@ -31,7 +37,13 @@
  *    §6.5; eps is the layer norm's variance epsilon (Deep Dive §6.2).
  *  - The LL layout (8 bytes of payload and an 8-byte flag in one 16-byte word,
  *    the reader checking the flag) is the LL protocol of "Every µs Matters",
- *    section on signalling without barriers.
+ *    section on signalling without barriers; the sentinel layout (a value
+ *    real data never takes marks an element not yet written, the buffer is
+ *    reset to it before reuse) is its sentinel mode and the one-shot
+ *    kernel's arrival test of Deep Dive §5.2, whose triple-buffered slots are
+ *    reset two calls ahead (the `reset` option).
+ *  - The pattern list (all-reduce only, with or without residual, FP8 or FP4
+ *    output, with or without the bf16 norm output) is Deep Dive §6.3.
  *
  * Conventions for every entry point:
  *  - Pointers marked (device) are HIP device pointers; (host) are host memory.
@@ -60,6 +72,9 @@ extern "C" {
 /* Largest supported rank count and row width. */
 #define ARFUSE_MAX_PARTIALS 8
 #define ARFUSE_MAX_D 65536
+/* Largest accepted opts->max_polls: bounds how long a row can wait on data
+ * that never arrives (each re-read follows a sleep of about 60 ns). */
+#define ARFUSE_MAX_POLLS (1u << 20)
 
 typedef enum {
   ARFUSE_OK = 0,
@@ -84,10 +99,19 @@ typedef enum {
                                  bf16 elements (element 4w first, little
                                  endian), bytes 8..15 a little-endian uint64
                                  flag; t*d*4 bytes per partial */
+#define ARFUSE_LAYOUT_SENTINEL 2 /* bf16 [t][d] like PLAIN; a 16-byte vector (8
+                                   elements) holding the sentinel pattern in
+                                   any element has not arrived yet */
+
+/* Default sentinel: a negative NaN bf16 pattern, which finite data never
+ * takes. (+0.0 or any finite value must not be used as a sentinel.) */
+#define ARFUSE_SENTINEL_DEFAULT 0xFFFFu
 
 /* Outputs of one call (the epilogue), as bit flags. */
 #define ARFUSE_EPI_BF16 1 /* out: bf16 y */
 #define ARFUSE_EPI_FP4 2  /* fp4_out + fp4_scales */
+#define ARFUSE_EPI_FP8 4  /* opts->fp8_out (not together with FP4) */
+/* A mask of 0 is the all-reduce alone (no gamma): only residual_out. */
 
 /* Device-side status of an LL call. The caller zeroes it before the call
  * (the library only ever ORs into code and adds to bad_words, so one word
@@ -95,22 +119,37 @@ typedef enum {
 typedef struct {
   uint32_t code;      /* 0, or ARFUSE_ERR_FLAG_TIMEOUT */
   uint32_t reserved;
-  uint64_t bad_words; /* LL words whose flag never matched */
+  uint64_t bad_words; /* LL words whose flag never matched, or, in the
+                         sentinel layout, 16-byte vectors that still held the
+                         sentinel after the last re-read */
 } arfuse_ll_status;
 
 /* Options of arfuse_rmsnorm_ex. Zero-initialise it for the defaults
  * (plain layout, library-chosen launch). */
 typedef struct {
-  int32_t layout;             /* ARFUSE_LAYOUT_PLAIN or ARFUSE_LAYOUT_LL */
-  uint32_t max_polls;         /* LL: re-reads of a word whose flag does not
-                                 match, with a short sleep between them,
-                                 before it counts as bad (0: check once) */
+  int32_t layout;             /* ARFUSE_LAYOUT_PLAIN, _LL or _SENTINEL */
+  uint32_t max_polls;         /* LL / SENTINEL: re-reads of a word or vector
+                                 that has not arrived, with a short sleep
+                                 between them, before it counts as bad
+                                 (0: check once); at most ARFUSE_MAX_POLLS */
   uint64_t ll_flag;           /* LL: the flag every word must carry */
   arfuse_ll_status* status;   /* LL: (device) status word, or NULL */
   int32_t block_threads;      /* launch override: threads per row block,
                                  a multiple of 64 in [64, 1024]; 0 = auto */
   int32_t vpt;                /* launch override: 16-byte vectors per thread
                                  per partial, 1, 2, 4 or 8; 0 = auto */
+  uint32_t sentinel;          /* SENTINEL: 16-bit pattern of a not-yet-
+                                 written element; 0 = ARFUSE_SENTINEL_DEFAULT */
+  uint32_t reserved;          /* must be 0 */
+  void* const* reset;         /* SENTINEL: (host) array of n_partials (device)
+                                 bf16 [t][d] buffers, 16-byte aligned, that this
+                                 call fills with the sentinel (the slot set a
+                                 later call reuses); or NULL */
+  uint8_t* fp8_out;           /* (device) uint8 [t][d] FP8 E4M3 codes of
+                                 y * fp8_inv_scale (sign bit 7, saturating at
+                                 448), 16-byte aligned; or NULL */
+  float fp8_inv_scale;        /* per-tensor reciprocal FP8 scale, finite */
+  uint32_t reserved2;         /* must be 0 */
 } arfuse_opts;
 
 /* The launch the library would use for a call. */
@@ -126,13 +165,17 @@ typedef struct {
  *  partials      (host) array of n_partials pointers; each (device) bf16
  *                [t][d], 16-byte aligned. Summed in array order.
  *  n_partials    1..8
- *  residual      (device) bf16 [t][d], 16-byte aligned
- *  gamma         (device) fp32 [d], 16-byte aligned
+ *  residual      (device) bf16 [t][d], 16-byte aligned; NULL: no residual
+ *                add (h is the rank sum)
+ *  gamma         (device) fp32 [d], 16-byte aligned; NULL: no RMSNorm (the
+ *                plain all-reduce); then out and the FP4/FP8 outputs must be
+ *                NULL and residual_out must be given
  *  eps           finite, >= 0; added to the mean square inside the root
  *  out           (device) bf16 [t][d] normalized output, 16-byte aligned;
- *                may be NULL only when fp4_out is given
+ *                or NULL
  *  residual_out  (device) bf16 [t][d] = bf16(h); may equal residual (in place)
- *                but must not otherwise overlap any other buffer
+ *                but must not otherwise overlap any other buffer; may be NULL
+ *                when gamma is given and another output is requested
  *  fp4_out       (device) uint8 [t][d/2] E2M1 codes, element 2k in the low
  *                nibble of byte k; 16-byte aligned; or NULL
  *  fp4_scales    (device) uint8 [t][d/16] E4M3 codes of the block scales;
@@ -150,9 +193,13 @@ int arfuse_rmsnorm(const void* const* partials, int n_partials, const void* resi
  * arfuse_rmsnorm_ex — as arfuse_rmsnorm, with options (opts may be NULL).
  * With opts->layout == ARFUSE_LAYOUT_LL every partial is (device) LL words
  * [t][d/4][16 bytes]; each word's flag is compared with opts->ll_flag and a
- * word that does not match is re-read up to opts->max_polls times. Words that
- * never match are counted into opts->status (if given); the rows holding
- * them get unspecified outputs. The kernel never waits without bound.
+ * word that does not match is re-read up to opts->max_polls times. With
+ * ARFUSE_LAYOUT_SENTINEL the partials are plain bf16 and a 16-byte vector
+ * holding opts->sentinel in any element is re-read the same way; opts->reset,
+ * if given, names buffers the call fills with the sentinel. Words or vectors
+ * that never arrive are counted into opts->status (if given); the rows
+ * holding them get unspecified outputs. The kernel never waits without
+ * bound. opts->fp8_out requests the FP8 output.
  */
 int arfuse_rmsnorm_ex(const void* const* partials, int n_partials, const void* residual,
                       const float* gamma, float eps, void* out, void* residual_out,

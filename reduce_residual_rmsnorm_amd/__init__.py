@@ -22,10 +22,14 @@ ARFUSE_ERR_LAUNCH = 3
 ARFUSE_ERR_FLAG_TIMEOUT = 4
 ARFUSE_LAYOUT_PLAIN = 0
 ARFUSE_LAYOUT_LL = 1
+ARFUSE_LAYOUT_SENTINEL = 2
+ARFUSE_SENTINEL_DEFAULT = 0xFFFF
+ARFUSE_EPI_FP8 = 4
 ARFUSE_EPI_BF16 = 1
 ARFUSE_EPI_FP4 = 2
 ARFUSE_MAX_PARTIALS = 8
 ARFUSE_MAX_D = 65536
+ARFUSE_MAX_POLLS = 1 << 20
 
 # The exported functions, as declared in include/arfuse.h.
 EXPORTED = ("arfuse_rmsnorm", "arfuse_rmsnorm_ex", "arfuse_quantize_fp4", "arfuse_query_launch",
@@ -51,7 +55,10 @@ class arfuse_ll_status(ctypes.Structure):
 class arfuse_opts(ctypes.Structure):
     _fields_ = [("layout", ctypes.c_int32), ("max_polls", ctypes.c_uint32),
                 ("ll_flag", ctypes.c_uint64), ("status", ctypes.c_void_p),
-                ("block_threads", ctypes.c_int32), ("vpt", ctypes.c_int32)]
+                ("block_threads", ctypes.c_int32), ("vpt", ctypes.c_int32),
+                ("sentinel", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("reset", ctypes.c_void_p), ("fp8_out", ctypes.c_void_p),
+                ("fp8_inv_scale", ctypes.c_float), ("reserved2", ctypes.c_uint32)]
 
 
 class arfuse_launch_info(ctypes.Structure):
@@ -117,9 +124,20 @@ def _stream(stream) -> int:
 
 
 def _opts(layout=ARFUSE_LAYOUT_PLAIN, ll_flag=0, max_polls=0, status=None, block_threads=0,
-          vpt=0) -> arfuse_opts:
-    return arfuse_opts(layout=int(layout), max_polls=int(max_polls), ll_flag=int(ll_flag),
-                       status=_addr(status), block_threads=int(block_threads), vpt=int(vpt))
+          vpt=0, sentinel=0, reset=None, fp8_out=None, fp8_inv_scale=1.0):
+    """Build an arfuse_opts; returns (opts, keepalive) - the host array of
+    reset pointers must outlive the call."""
+    keep = None
+    reset_addr = 0
+    if reset is not None:
+        keep = (ctypes.c_void_p * len(reset))(*[_addr(r) for r in reset])
+        reset_addr = ctypes.addressof(keep)
+    o = arfuse_opts(layout=int(layout), max_polls=int(max_polls), ll_flag=int(ll_flag),
+                    status=_addr(status), block_threads=int(block_threads), vpt=int(vpt),
+                    sentinel=int(sentinel), reserved=0, reset=reset_addr,
+                    fp8_out=_addr(fp8_out), fp8_inv_scale=float(fp8_inv_scale), reserved2=0)
+    o._keep = keep
+    return o
 
 
 def _check(rc: int, where: str) -> None:
@@ -150,11 +168,15 @@ def arfuse_rmsnorm(partials: Sequence, residual, gamma, eps: float, out, residua
 def arfuse_rmsnorm_ex(partials: Sequence, residual, gamma, eps: float, out, residual_out,
                       fp4_out=None, fp4_scales=None, stream=None, t=None, d=None, *,
                       layout=ARFUSE_LAYOUT_PLAIN, ll_flag=0, max_polls=0, status=None,
-                      block_threads=0, vpt=0) -> None:
-    """Fused call with options; see arfuse_rmsnorm_ex in include/arfuse.h."""
+                      block_threads=0, vpt=0, sentinel=0, reset=None, fp8_out=None,
+                      fp8_inv_scale=1.0) -> None:
+    """Fused call with options; see arfuse_rmsnorm_ex in include/arfuse.h.
+    residual and gamma may be None (the no-residual and all-reduce-only
+    patterns); then pass t and d explicitly."""
     t, d = _td(residual, t, d)
     arr = (ctypes.c_void_p * len(partials))(*[_addr(p) for p in partials])
-    o = _opts(layout, ll_flag, max_polls, status, block_threads, vpt)
+    o = _opts(layout, ll_flag, max_polls, status, block_threads, vpt, sentinel, reset, fp8_out,
+              fp8_inv_scale)
     rc = lib.arfuse_rmsnorm_ex(arr, len(partials), _addr(residual), _addr(gamma), float(eps),
                                _addr(out), _addr(residual_out), _addr(fp4_out),
                                _addr(fp4_scales), t, d, _stream(stream), ctypes.byref(o))

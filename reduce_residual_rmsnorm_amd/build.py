@@ -3,6 +3,10 @@
     python reduce_residual_rmsnorm_amd/build.py
 
 (Run it as a file: importing the package loads the library it builds.)
+
+The row-kernel instances are compiled per rank count N (``arfuse_rows.hip``
+with ``-DARFUSE_N=1..8``) in parallel with the host ABI unit
+(``arfuse.hip``), then linked into one library.
 """
 
 from __future__ import annotations
@@ -10,10 +14,14 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "arfuse.hip")
+CSRC = os.path.join(PKG, "csrc")
+SRC = os.path.join(CSRC, "arfuse.hip")
+ROWS = os.path.join(CSRC, "arfuse_rows.hip")
+DEVICE = os.path.join(CSRC, "arfuse_device.hpp")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libarfuse.so")
@@ -25,7 +33,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # no packed-fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # the rank sum must be plain IEEE adds in order; division and sqrt correctly rounded
@@ -37,17 +44,42 @@ FLAGS = [
 ]
 
 
+def _jobs():
+    units = [(SRC, [], "arfuse")]
+    units += [(ROWS, ["-DARFUSE_N=%d" % n], "rows_n%d" % n) for n in range(1, 9)]
+    return units
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(LIBDIR, exist_ok=True)
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-o", tmp, SRC]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building %s" % SRC)
-    os.replace(tmp, LIB)
+    with tempfile.TemporaryDirectory(prefix="arfuse_build_") as tmpdir:
+        procs = []
+        for src, defs, name in _jobs():
+            obj = os.path.join(tmpdir, name + ".o")
+            cmd = [HIPCC, *FLAGS, *defs, "-I", INCLUDE, "-I", CSRC, "-c", "-o", obj, src]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                           text=True), obj, src))
+        objs = []
+        failed = False
+        for p, obj, src in procs:
+            out, _ = p.communicate()
+            if p.returncode != 0:
+                sys.stderr.write(out)
+                failed = True
+            objs.append(obj)
+        if failed:
+            raise RuntimeError("hipcc failed building %s" % CSRC)
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("hipcc failed linking %s" % LIB)
+        os.replace(tmp, LIB)
     return LIB
 
 
@@ -55,9 +87,9 @@ def is_stale() -> bool:
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    deps = [SRC, os.path.join(INCLUDE, "arfuse.h")]
+    deps = [SRC, ROWS, DEVICE, os.path.join(INCLUDE, "arfuse.h")]
     return any(os.path.getmtime(p) > t for p in deps)
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose="-v" in sys.argv))

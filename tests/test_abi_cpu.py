@@ -77,10 +77,7 @@ INVALID = {
     "n_nine": dict(parts=[spaced(i) for i in range(9)]),
     "null_partial": dict(parts=[spaced(0), 0]),
     "misaligned_partial": dict(parts=[spaced(0) + 8]),
-    "null_residual": dict(residual=0),
     "null_gamma": dict(gamma=0),
-    "null_residual_out": dict(residual_out=0),
-    "no_output": dict(out=0),
     "misaligned_out": dict(out=spaced(10) + 4),
     "fp4_without_scales": dict(fp4=spaced(12)),
     "scales_without_fp4": dict(scales=spaced(13)),
@@ -98,12 +95,55 @@ INVALID = {
     "out_overlaps_gamma": dict(out=spaced(9) - PLANE + 16),
     "fp4_overlaps_out": dict(fp4=spaced(10) + 16, scales=spaced(13)),
     "scales_overlap_fp4": dict(fp4=spaced(12), scales=spaced(12) + 16),
+    "norm_output_without_gamma": dict(gamma=0),
+    "allreduce_without_residual_out": dict(gamma=0, out=0, residual_out=0),
+    "misaligned_residual": dict(residual=spaced(8) + 2),
+    "nothing_to_write": dict(out=0, residual_out=0),
 }
 
 
 @pytest.mark.parametrize("case", sorted(INVALID))
 def test_invalid_arguments_rejected(case):
     assert call(**good(**INVALID[case])) == arf.ARFUSE_ERR_INVALID_ARG
+
+
+def test_patterns_accepted_at_t_zero_and_rejected_when_inconsistent():
+    # all-reduce only: no gamma, no norm outputs, residual_out present
+    assert call(**good(gamma=0, out=0, t=0)) == arf.ARFUSE_OK
+    # no residual, norm outputs only
+    assert call(**good(residual=0, residual_out=0, t=0)) == arf.ARFUSE_OK
+    # FP8 options
+    o = arf._opts(fp8_out=spaced(13), fp8_inv_scale=float("inf"))
+    assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
+    o = arf._opts(fp8_out=spaced(13), fp8_inv_scale=2.0)
+    assert call(**good(fp4=spaced(12), scales=spaced(14), opts=o)) == arf.ARFUSE_ERR_UNSUPPORTED
+    o = arf._opts(fp8_out=spaced(10) + 16, fp8_inv_scale=2.0)   # overlaps out
+    assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
+
+
+def test_sentinel_options_validated():
+    S = arf.ARFUSE_LAYOUT_SENTINEL
+    assert call(**good(opts=arf._opts(layout=3))) == arf.ARFUSE_ERR_INVALID_ARG
+    # reset buffers only with the sentinel layout
+    o = arf._opts(reset=[spaced(20 + i) for i in range(4)])
+    assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
+    o = arf._opts(layout=S, sentinel=0x1FFFF)
+    assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
+    # a reset buffer overlapping a partial, or missing
+    o = arf._opts(layout=S, reset=[spaced(0)] + [spaced(21 + i) for i in range(3)])
+    assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
+    o = arf._opts(layout=S, reset=[0] + [spaced(21 + i) for i in range(3)])
+    assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
+    o = arf._opts(layout=S, reset=[spaced(20 + i) for i in range(4)])
+    assert call(**good(opts=o, t=0)) == arf.ARFUSE_OK
+    o = arf._opts()
+    o.reserved = 1
+    assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
+    # the re-read bound
+    o = arf._opts(layout=S, max_polls=arf.ARFUSE_MAX_POLLS)
+    assert call(**good(opts=o, t=0)) == arf.ARFUSE_OK
+    o = arf._opts(layout=S, max_polls=arf.ARFUSE_MAX_POLLS + 1)
+    assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
 
 
 def test_unsupported_width():
@@ -119,7 +159,7 @@ def test_t_zero_is_a_noop():
 
 
 def test_bad_options_rejected():
-    o = arf._opts(layout=2)
+    o = arf._opts(layout=7)
     assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
     for bt in (32, 100, 2048):
         assert call(**good(opts=arf._opts(block_threads=bt))) == arf.ARFUSE_ERR_INVALID_ARG
