@@ -144,7 +144,9 @@ typedef struct {
   void* const* reset;         /* SENTINEL: (host) array of n_partials (device)
                                  bf16 [t][d] buffers, 16-byte aligned, that this
                                  call fills with the sentinel (the slot set a
-                                 later call reuses); or NULL */
+                                 later call reuses); or NULL. For t <= 128
+                                 extra workgroups of the same launch write
+                                 them, otherwise each row's workgroup does */
   uint8_t* fp8_out;           /* (device) uint8 [t][d] FP8 E4M3 codes of
                                  y * fp8_inv_scale (sign bit 7, saturating at
                                  448), 16-byte aligned; or NULL */
@@ -154,7 +156,9 @@ typedef struct {
 
 /* The launch the library would use for a call. */
 typedef struct {
-  int64_t grid;         /* workgroups (one token row each) */
+  int64_t grid;         /* workgroups: one per token row, plus, in the
+                           sentinel layout with a reset set and t <= 128,
+                           the blocks that write the reset */
   int32_t block;        /* threads per workgroup */
   int32_t vpt;          /* 16-byte vectors per thread per partial */
 } arfuse_launch_info;

@@ -73,16 +73,16 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* src, u32x4* dst,
 
 // ------------------------------------------------------------ dispatch
 
-RowFn select_row_kernel(int n, int vpt, bool ll, int epi) {
+RowFn select_row_kernel(int n, int vpt, int layout, int epi) {
   switch (n) {
-    case 1: return select_row_kernel_n1(vpt, ll, epi);
-    case 2: return select_row_kernel_n2(vpt, ll, epi);
-    case 3: return select_row_kernel_n3(vpt, ll, epi);
-    case 4: return select_row_kernel_n4(vpt, ll, epi);
-    case 5: return select_row_kernel_n5(vpt, ll, epi);
-    case 6: return select_row_kernel_n6(vpt, ll, epi);
-    case 7: return select_row_kernel_n7(vpt, ll, epi);
-    case 8: return select_row_kernel_n8(vpt, ll, epi);
+    case 1: return select_row_kernel_n1(vpt, layout, epi);
+    case 2: return select_row_kernel_n2(vpt, layout, epi);
+    case 3: return select_row_kernel_n3(vpt, layout, epi);
+    case 4: return select_row_kernel_n4(vpt, layout, epi);
+    case 5: return select_row_kernel_n5(vpt, layout, epi);
+    case 6: return select_row_kernel_n6(vpt, layout, epi);
+    case 7: return select_row_kernel_n7(vpt, layout, epi);
+    case 8: return select_row_kernel_n8(vpt, layout, epi);
   }
   return nullptr;
 }
@@ -133,6 +133,20 @@ int choose_launch(int64_t d8, const arfuse_opts* o, int* block, int* vpt) {
   *block = b;
   *vpt = v;
   return ARFUSE_OK;
+}
+
+// Sentinel layout with a reset set: up to this many rows, the rows leave the
+// reset to extra blocks of the same launch (the rows occupy at most half of
+// the 256 CUs, so the reset stores run on CUs that would otherwise idle);
+// above it every row block refills its own row.
+constexpr int64_t kSpreadResetRows = 128;
+
+// Extra reset blocks of a call: N planes of t * d / 8 vectors, one vector per
+// thread. 0 when the rows do the reset themselves or there is none.
+int64_t reset_blocks(int n, int64_t t, int64_t d, int block, bool reset) {
+  if (!reset || t > kSpreadResetRows) return 0;
+  const int64_t plane_vecs = t * d / 8;
+  return (int64_t)n * ((plane_vecs + block - 1) / block);
 }
 
 int check_shape(int n, int64_t t, int64_t d, int epi) {
@@ -238,13 +252,17 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
   a.fp8_inv_scale = fp8_out ? opts->fp8_inv_scale : 1.0f;
   a.max_polls = opts ? opts->max_polls : 0;
   a.sentinel2 = spat | (spat << 16);
+  const int64_t extra = reset_blocks(n, t, d, block, reset != nullptr);
   a.flags = (residual ? kHasResidual : 0u) | (residual_out ? kHasResidualOut : 0u) |
-            (sentinel ? kSentinel : 0u) | (reset ? kReset : 0u);
+            ((reset && extra == 0) ? kReset : 0u);
+  a.rows = (uint32_t)t;
+  a.plane_vecs = (uint32_t)(t * d / 8);  // only read by reset blocks: t <= 128
+  a.reset_bpp = (uint32_t)((t * d / 8 + block - 1) / block);
 
-  const void* fn = (const void*)select_row_kernel(n, vpt, ll, epi);
+  const void* fn = (const void*)select_row_kernel(n, vpt, layout, epi);
   if (!fn) return ARFUSE_ERR_UNSUPPORTED;
   void* args[] = {&a};
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)t), dim3((unsigned)block), args, 0,
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(t + extra)), dim3((unsigned)block), args, 0,
                                  (hipStream_t)stream);
   return launch_status(e);
 }
@@ -303,7 +321,8 @@ int arfuse_query_launch(int n_partials, int64_t t, int64_t d, int epilogue,
   int block = 0, vpt = 0;
   rc = choose_launch(d / 8, opts, &block, &vpt);
   if (rc) return rc;
-  info->grid = t;
+  const bool reset = opts && opts->layout == ARFUSE_LAYOUT_SENTINEL && opts->reset;
+  info->grid = t + reset_blocks(n_partials, t, d, block, reset);
   info->block = block;
   info->vpt = vpt;
   return ARFUSE_OK;
@@ -317,9 +336,11 @@ int arfuse_launch_floor(int n_partials, int64_t t, int64_t d, int epilogue,
   rc = choose_launch(d / 8, opts, &block, &vpt);
   if (rc) return rc;
   if (t == 0) return ARFUSE_OK;
+  const bool reset = opts && opts->layout == ARFUSE_LAYOUT_SENTINEL && opts->reset;
+  const int64_t grid = t + reset_blocks(n_partials, t, d, block, reset);
   RowArgs a = {};
   void* args[] = {&a};
-  hipError_t e = hipLaunchKernel((const void*)floor_kernel, dim3((unsigned)t), dim3((unsigned)block),
+  hipError_t e = hipLaunchKernel((const void*)floor_kernel, dim3((unsigned)grid), dim3((unsigned)block),
                                  args, 0, (hipStream_t)stream);
   return launch_status(e);
 }

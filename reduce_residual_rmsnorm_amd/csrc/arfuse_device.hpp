@@ -37,15 +37,21 @@ struct RowArgs {
   float fp8_inv_scale;
   uint32_t max_polls;
   uint32_t sentinel2;  // sentinel pattern in both halves of a dword
-  uint32_t flags;      // kHasResidual | kHasResidualOut | kSentinel | kReset
+  uint32_t flags;      // kHasResidual | kHasResidualOut | kReset
+  // sentinel layout, reset by extra blocks (few rows): blocks at and past
+  // `rows` each refill one block-sized chunk of one slot plane
+  uint32_t rows;        // t
+  uint32_t plane_vecs;  // 16-byte vectors per slot plane (t * d / 8)
+  uint32_t reset_bpp;   // reset blocks per plane (plane_vecs / block, rounded up)
 };
 
 // RowArgs.flags. These features do not change the kernel's shape, so they are
-// workgroup-uniform runtime branches rather than more template instances.
+// workgroup-uniform runtime branches rather than more template instances. (The
+// sentinel check is a template parameter instead: its compares would otherwise
+// sit in every plain instance.)
 constexpr uint32_t kHasResidual = 1u;
 constexpr uint32_t kHasResidualOut = 2u;
-constexpr uint32_t kSentinel = 4u;   // plain geometry: check arrival per vector
-constexpr uint32_t kReset = 8u;      // refill a.reset[] with the sentinel
+constexpr uint32_t kReset = 8u;      // sentinel layout: each row block refills its row of a.reset[]
 
 // Epilogue mask (template parameter EPI): ARFUSE_EPI_BF16 | _FP4 | _FP8;
 // 0 = no RMSNorm, the all-reduce alone.
@@ -116,19 +122,28 @@ struct E2M1Thresholds {
 __device__ __forceinline__ E2M1Thresholds e2m1_thresholds(float s) {
   // s == 0: every magnitude is 0, which +inf thresholds give for finite |y|
   const float ss = (s != 0.0f) ? s : __builtin_inff();
-  return E2M1Thresholds{{ss * 0.25f, ss * 0.75f, ss * 1.25f, ss * 1.75f, ss * 2.5f, ss * 3.5f,
-                         ss * 5.0f}};
+  E2M1Thresholds th{{ss * 0.25f, ss * 0.75f, ss * 1.25f, ss * 1.75f, ss * 2.5f, ss * 3.5f,
+                     ss * 5.0f}};
+  // Keep the seven products in registers: otherwise the compiler rewrites
+  // each element's threshold select as a multiply of s by a selected
+  // constant and turns the nested selects into divergent branches.
+#pragma unroll
+  for (int i = 0; i < 7; ++i) asm("" : "+v"(th.t[i]));
+  return th;
 }
 
 // The magnitude is the number of thresholds |y| passes (strictly for the
 // ties that round down, t[0], t[2], t[4], t[6]); the thresholds ascend, so
 // three comparisons find it: t[3] splits {0..3} from {4..7}, then t[1] or
-// t[5], then one of the strict ones.
+// t[5], then one of the strict ones. Selects only, no branches.
 __device__ __forceinline__ uint32_t e2m1_rne(float a, const E2M1Thresholds& th) {
   const bool b2 = a >= th.t[3];
-  const bool b1 = a >= (b2 ? th.t[5] : th.t[1]);
-  const float tl = b2 ? (b1 ? th.t[6] : th.t[4]) : (b1 ? th.t[2] : th.t[0]);
-  return (b2 ? 4u : 0u) + (b1 ? 2u : 0u) + (a > tl ? 1u : 0u);
+  const float mid = b2 ? th.t[5] : th.t[1];
+  const bool b1 = a >= mid;
+  const float lo = b1 ? th.t[2] : th.t[0];
+  const float hi = b1 ? th.t[6] : th.t[4];
+  const float tl = b2 ? hi : lo;
+  return (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (a > tl ? 1u : 0u);
 }
 
 // FP4 of the 8 values a lane holds. Lanes (2m, 2m+1) hold one 16-element
@@ -301,7 +316,7 @@ __device__ __forceinline__ T* at_w(char* base, uint32_t off) {
   return reinterpret_cast<T*>(base + off);
 }
 
-template <int N, int VPT, bool LL, int EPI>
+template <int N, int VPT, bool LL, bool SENT, int EPI>
 __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   constexpr bool NORM = EPI != 0;
   constexpr bool OUT = (EPI & ARFUSE_EPI_BF16) != 0;
@@ -309,6 +324,18 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   constexpr bool FP8 = (EPI & ARFUSE_EPI_FP8) != 0;
   const int lane = threadIdx.x;
   const int nthr = blockDim.x;
+  if constexpr (SENT) {
+    // a reset block (only launched when the rows are few): refill one chunk
+    // of one slot plane of the set a later call reuses, a vector per lane,
+    // on a CU that no row occupies
+    if (blockIdx.x >= a.rows) {
+      const uint32_t b = blockIdx.x - a.rows;
+      const uint32_t i = b / a.reset_bpp;
+      const uint32_t v = (b - i * a.reset_bpp) * (uint32_t)nthr + (uint32_t)lane;
+      if (v < a.plane_vecs) store16(a.reset[i] + v, u32x4{a.sentinel2, a.sentinel2, a.sentinel2, a.sentinel2});
+      return;
+    }
+  }
   const uint32_t d = (uint32_t)(a.d8 * 8);
   const int64_t rb = (int64_t)blockIdx.x * d;  // first element of the row
   const bool has_res = (a.flags & kHasResidual) != 0;
@@ -406,7 +433,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
               raw[k][i][j] = ll_repoll(at<u32x4>(prow[i], eo[k][j] * 4), raw[k][i][j], a.ll_flag,
                                        a.max_polls, &bad);
     }
-  } else if (a.flags & kSentinel) {
+  } else if constexpr (SENT) {
     bool any = false;
 #pragma unroll
     for (int k = 0; k < VPT; ++k)
@@ -552,14 +579,15 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
 
 typedef void (*RowFn)(RowArgs);
 
-// Instances for one rank count: returns the kernel for (VPT, layout, EPI).
-RowFn select_row_kernel_n1(int vpt, bool ll, int epi);
-RowFn select_row_kernel_n2(int vpt, bool ll, int epi);
-RowFn select_row_kernel_n3(int vpt, bool ll, int epi);
-RowFn select_row_kernel_n4(int vpt, bool ll, int epi);
-RowFn select_row_kernel_n5(int vpt, bool ll, int epi);
-RowFn select_row_kernel_n6(int vpt, bool ll, int epi);
-RowFn select_row_kernel_n7(int vpt, bool ll, int epi);
-RowFn select_row_kernel_n8(int vpt, bool ll, int epi);
+// Instances for one rank count: returns the kernel for (VPT, layout, EPI);
+// layout is ARFUSE_LAYOUT_PLAIN, _LL or _SENTINEL.
+RowFn select_row_kernel_n1(int vpt, int layout, int epi);
+RowFn select_row_kernel_n2(int vpt, int layout, int epi);
+RowFn select_row_kernel_n3(int vpt, int layout, int epi);
+RowFn select_row_kernel_n4(int vpt, int layout, int epi);
+RowFn select_row_kernel_n5(int vpt, int layout, int epi);
+RowFn select_row_kernel_n6(int vpt, int layout, int epi);
+RowFn select_row_kernel_n7(int vpt, int layout, int epi);
+RowFn select_row_kernel_n8(int vpt, int layout, int epi);
 
 }  // namespace arfuse_detail

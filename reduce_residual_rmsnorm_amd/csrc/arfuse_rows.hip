@@ -1,5 +1,5 @@
 // Row-kernel instances for one rank count ARFUSE_N (set by the build):
-// every VPT in {1, 2, 4, 8} x {plain, LL} x epilogue mask.
+// every VPT in {1, 2, 4, 8} x {plain, LL, sentinel} x epilogue mask.
 
 #include "arfuse_device.hpp"
 
@@ -13,39 +13,45 @@
 namespace arfuse_detail {
 namespace {
 
-template <int N, int VPT, bool LL>
+template <int N, int VPT, bool LL, bool SENT>
 RowFn by_epi(int epi) {
+  constexpr int B = ARFUSE_EPI_BF16, F4 = ARFUSE_EPI_FP4, F8 = ARFUSE_EPI_FP8;
   switch (epi) {
-    case 0: return row_kernel<N, VPT, LL, 0>;
-    case ARFUSE_EPI_BF16: return row_kernel<N, VPT, LL, ARFUSE_EPI_BF16>;
-    case ARFUSE_EPI_FP4: return row_kernel<N, VPT, LL, ARFUSE_EPI_FP4>;
-    case ARFUSE_EPI_BF16 | ARFUSE_EPI_FP4: return row_kernel<N, VPT, LL, ARFUSE_EPI_BF16 | ARFUSE_EPI_FP4>;
-    case ARFUSE_EPI_FP8: return row_kernel<N, VPT, LL, ARFUSE_EPI_FP8>;
-    case ARFUSE_EPI_BF16 | ARFUSE_EPI_FP8: return row_kernel<N, VPT, LL, ARFUSE_EPI_BF16 | ARFUSE_EPI_FP8>;
+    case 0: return row_kernel<N, VPT, LL, SENT, 0>;
+    case B: return row_kernel<N, VPT, LL, SENT, B>;
+    case F4: return row_kernel<N, VPT, LL, SENT, F4>;
+    case B | F4: return row_kernel<N, VPT, LL, SENT, B | F4>;
+    case F8: return row_kernel<N, VPT, LL, SENT, F8>;
+    case B | F8: return row_kernel<N, VPT, LL, SENT, B | F8>;
   }
   return nullptr;
 }
 
 template <int N, int VPT>
-RowFn by_layout(bool ll, int epi) {
-  return ll ? by_epi<N, VPT, true>(epi) : by_epi<N, VPT, false>(epi);
+RowFn by_layout(int layout, int epi) {
+  switch (layout) {
+    case ARFUSE_LAYOUT_PLAIN: return by_epi<N, VPT, false, false>(epi);
+    case ARFUSE_LAYOUT_LL: return by_epi<N, VPT, true, false>(epi);
+    case ARFUSE_LAYOUT_SENTINEL: return by_epi<N, VPT, false, true>(epi);
+  }
+  return nullptr;
 }
 
 template <int N>
-RowFn by_vpt(int vpt, bool ll, int epi) {
+RowFn by_vpt(int vpt, int layout, int epi) {
   switch (vpt) {
-    case 1: return by_layout<N, 1>(ll, epi);
-    case 2: return by_layout<N, 2>(ll, epi);
-    case 4: return by_layout<N, 4>(ll, epi);
-    case 8: return by_layout<N, 8>(ll, epi);
+    case 1: return by_layout<N, 1>(layout, epi);
+    case 2: return by_layout<N, 2>(layout, epi);
+    case 4: return by_layout<N, 4>(layout, epi);
+    case 8: return by_layout<N, 8>(layout, epi);
   }
   return nullptr;
 }
 
 }  // namespace
 
-RowFn ARFUSE_CAT(select_row_kernel_n, ARFUSE_N)(int vpt, bool ll, int epi) {
-  return by_vpt<ARFUSE_N>(vpt, ll, epi);
+RowFn ARFUSE_CAT(select_row_kernel_n, ARFUSE_N)(int vpt, int layout, int epi) {
+  return by_vpt<ARFUSE_N>(vpt, layout, epi);
 }
 
 }  // namespace arfuse_detail
