@@ -196,6 +196,16 @@ __device__ __forceinline__ bool holds_sentinel(u32x4 w, uint32_t s2) {
          ((w.w & 0xFFFFu) == lo) | ((w.w & 0xFFFF0000u) == hi);
 }
 
+// Sentinel layout, patterns that are not NaN: nonzero iff some 16-bit half of
+// the vector equals the pattern. Per dword t = w ^ s2, a half of t is zero
+// iff (t - 0x00010001) & ~t has that half's top bit set; a borrow out of a
+// zero low half can only flag the high half when the low one already is.
+__device__ __forceinline__ uint32_t zero_half4(u32x4 w, uint32_t s2) {
+  const uint32_t a = w.x ^ s2, b = w.y ^ s2, c = w.z ^ s2, d = w.w ^ s2;
+  return (((a - 0x00010001u) & ~a) | ((b - 0x00010001u) & ~b) | ((c - 0x00010001u) & ~c) |
+          ((d - 0x00010001u) & ~d)) & 0x80008000u;
+}
+
 // Re-read a vector that still holds the sentinel, bounded like ll_repoll.
 __device__ __forceinline__ u32x4 sentinel_repoll(const u32x4* p, u32x4 w, uint32_t s2,
                                                  uint32_t max_polls, uint32_t* bad) {
@@ -400,7 +410,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
         rres[k] = load16<true>(at<u32x4>(rrow, eo[k][0] * 2));
       }
     }
-    if constexpr (NORM) {
+    if constexpr (NORM && !SENT) {  // sentinel layout: after the arrival check
       g[k][0] = *at<f32x4>(grow, eo[k][0] * 4);
       g[k][1] = *at<f32x4>(grow, eo[k][1] * 4);
     }
@@ -409,11 +419,10 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   // of the row's loads are in flight before the first use
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- arrival: LL flags, or (plain geometry) the sentinel. One pass of
-  // compares; only a lane holding a word or vector that has not arrived takes
-  // the bounded re-poll path. Then unpack the payload.
+  // ---- arrival. LL: one pass of flag compares. Sentinel: a cheap filter
+  // first; only a lane that holds a word or vector that has not arrived runs
+  // the exact check and the bounded re-poll.
   uint32_t bad = 0;
-  u32x4 pv[VPT][N];
   if constexpr (LL) {
     bool all_ok = true;
 #pragma unroll
@@ -433,63 +442,93 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
               raw[k][i][j] = ll_repoll(at<u32x4>(prow[i], eo[k][j] * 4), raw[k][i][j], a.ll_flag,
                                        a.max_polls, &bad);
     }
-  } else if constexpr (SENT) {
-    bool any = false;
+  }
+  // exact sentinel check of every vector the lane owns, re-reading the
+  // pending ones (bounded)
+  auto sentinel_wait = [&]() {
 #pragma unroll
     for (int k = 0; k < VPT; ++k)
 #pragma unroll
-      for (int i = 0; i < N; ++i) any |= ok[k][0] && holds_sentinel(raw[k][i][0], a.sentinel2);
-    if (__builtin_expect(any, 0)) {
+      for (int i = 0; i < N; ++i)
+        if (ok[k][0] && holds_sentinel(raw[k][i][0], a.sentinel2))
+          raw[k][i][0] = sentinel_repoll(at<u32x4>(prow[i], eo[k][0] * 2), raw[k][i][0],
+                                         a.sentinel2, a.max_polls, &bad);
+  };
+  // refill this row of the slot set a later call reuses; done last, when the
+  // row's data no longer occupy registers
+  auto reset_row = [&]() {
+    if constexpr (SENT) {
+      if (a.flags & kReset) {
+        const u32x4 sv = {a.sentinel2, a.sentinel2, a.sentinel2, a.sentinel2};
 #pragma unroll
-      for (int k = 0; k < VPT; ++k)
+        for (int k = 0; k < VPT; ++k)
+          if (ok[k][0]) {
 #pragma unroll
-        for (int i = 0; i < N; ++i)
-          if (ok[k][0] && holds_sentinel(raw[k][i][0], a.sentinel2))
-            raw[k][i][0] = sentinel_repoll(at<u32x4>(prow[i], eo[k][0] * 2), raw[k][i][0],
-                                           a.sentinel2, a.max_polls, &bad);
+            for (int i = 0; i < N; ++i)
+              store16(at_w<u32x4>((char*)a.reset[i] + rb * 2, eo[k][0] * 2), sv);
+          }
+      }
     }
-    if (a.flags & kReset) {  // refill the slot set a later call reuses
-      const u32x4 sv = {a.sentinel2, a.sentinel2, a.sentinel2, a.sentinel2};
+  };
+  if constexpr (SENT) {
+    // The filter: a zero 16-bit half in (data XOR pattern), found with
+    // integer ops on whole dwords. (Per-element compares each write a lane
+    // mask that the scalar unit then has to combine, a long serial chain.)
+    uint32_t z = 0;
 #pragma unroll
-      for (int k = 0; k < VPT; ++k)
-        if (ok[k][0]) {
+    for (int k = 0; k < VPT; ++k) {
+      uint32_t zk = 0;
 #pragma unroll
-          for (int i = 0; i < N; ++i) store16(at_w<u32x4>((char*)a.reset[i] + rb * 2, eo[k][0] * 2), sv);
-        }
+      for (int i = 0; i < N; ++i) zk |= zero_half4(raw[k][i][0], a.sentinel2);
+      z |= ok[k][0] ? zk : 0u;
     }
-  }
+    if (__builtin_expect(z != 0, 0)) sentinel_wait();
+    if constexpr (NORM) {  // gamma is L2-resident; loading it here keeps the
+                           // re-poll path's registers free
 #pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      if constexpr (LL)
-        pv[k][i] = u32x4{raw[k][i][0].x, raw[k][i][0].y, raw[k][i][1].x, raw[k][i][1].y};
-      else
-        pv[k][i] = raw[k][i][0];
+      for (int k = 0; k < VPT; ++k) {
+        g[k][0] = *at<f32x4>(grow, eo[k][0] * 4);
+        g[k][1] = *at<f32x4>(grow, eo[k][1] * 4);
+      }
     }
   }
 
-  // ---- rank-ordered fp32 sum, residual last, residual_out, sum of squares
+  // ---- rank-ordered fp32 sum, residual last
   float h[VPT][8];
+  auto rank_sum = [&]() {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      u32x4 pv[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        if constexpr (LL)
+          pv[i] = u32x4{raw[k][i][0].x, raw[k][i][0].y, raw[k][i][1].x, raw[k][i][1].y};
+        else
+          pv[i] = raw[k][i][0];
+      }
+      float acc[8], f[8];
+      widen8(pv[0], acc);
+#pragma unroll
+      for (int i = 1; i < N; ++i) {
+        widen8(pv[i], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + f[e];
+      }
+      if (has_res) {
+        widen8(rres[k], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[k][e] = acc[e] + f[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[k][e] = acc[e];
+      }
+    }
+  };
+  rank_sum();
+  // ---- residual_out, sum of squares
   double ss = 0.0;
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    float acc[8], f[8];
-    widen8(pv[k][0], acc);
-#pragma unroll
-    for (int i = 1; i < N; ++i) {
-      widen8(pv[k][i], f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + f[e];
-    }
-    if (has_res) {
-      widen8(rres[k], f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[k][e] = acc[e] + f[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[k][e] = acc[e];
-    }
     if (has_rout) {
       const u32x4 hb = narrow8(h[k]);
       if constexpr (LL) {
@@ -510,7 +549,10 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     atomicAdd((unsigned long long*)&a.status->bad_words, (unsigned long long)bad);
     atomicOr(&a.status->code, (uint32_t)ARFUSE_ERR_FLAG_TIMEOUT);
   }
-  if constexpr (!NORM) return;
+  if constexpr (!NORM) {
+    reset_row();
+    return;
+  }
 
   // ---- row reduction: DPP tree inside each wave, one LDS slot per wave, then
   // every wave sums the (at most 16) slots with the same 16-lane tree
@@ -575,6 +617,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
       }
     }
   }
+  reset_row();
 }
 
 typedef void (*RowFn)(RowArgs);
