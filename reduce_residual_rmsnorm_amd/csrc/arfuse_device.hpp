@@ -424,14 +424,21 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   // the exact check and the bounded re-poll.
   uint32_t bad = 0;
   if constexpr (LL) {
-    bool all_ok = true;
+    // filter: OR of (flag XOR expected) over the lane's words, in vector
+    // integer ops (per-word compares would each make a lane mask for the
+    // scalar unit to combine)
+    const uint32_t flo = (uint32_t)a.ll_flag, fhi = (uint32_t)(a.ll_flag >> 32);
+    uint32_t mis = 0;
 #pragma unroll
     for (int k = 0; k < VPT; ++k)
 #pragma unroll
-      for (int i = 0; i < N; ++i)
+      for (int j = 0; j < 2; ++j) {
+        uint32_t m = 0;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) all_ok &= !ok[k][j] || ll_ok(raw[k][i][j], a.ll_flag);
-    if (__builtin_expect(!all_ok, 0)) {
+        for (int i = 0; i < N; ++i) m |= (raw[k][i][j].z ^ flo) | (raw[k][i][j].w ^ fhi);
+        mis |= ok[k][j] ? m : 0u;
+      }
+    if (__builtin_expect(mis != 0, 0)) {
 #pragma unroll
       for (int k = 0; k < VPT; ++k)
 #pragma unroll
