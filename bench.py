@@ -369,6 +369,11 @@ def recorded_traffic(workload: str):
 
 # ------------------------------------------------------------ profile summaries
 
+# One decode chain per row-kernel instance, so the trace's per-kernel rows
+# are one chain each.
+DECODE_PROFILED = ("decode_n8_t8_d8192_chain160", "decode_n8_t8_d8192_chain160_ll",
+                   "decode_n8_t8_d8192_chain160_sentinel", "fp4_n4_t1_d8192_x100")
+
 PROFILE_COMMANDS = {
     "trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
              "-d $REPO/gpurun_out/prof_trace -o prefill -- python3 $REPO/bench.py --steps 50 "
@@ -379,6 +384,9 @@ PROFILE_COMMANDS = {
     "pmc_copy": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {C} --kernel-include-regex "
                 "copy_kernel -f csv -d $REPO/gpurun_out/pmc_copy_{C} -o pmc -- python3 "
                 "$REPO/bench.py --copy-only",
+    "trace_decode": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
+                    "-d $REPO/gpurun_out/prof_decode -o decode -- python3 $REPO/bench.py "
+                    + " ".join("--only-extra " + x for x in DECODE_PROFILED),
 }
 
 
@@ -447,6 +455,85 @@ def summarize_profiles(outdir: str) -> None:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec, indent=1))
+    if os.path.exists(os.path.join(outdir, "prof_decode", "decode_kernel_stats.csv")):
+        summarize_decode_profile(outdir)
+
+
+def summarize_decode_profile(outdir: str) -> None:
+    """profiles/row_kernel_decode_chains_stats.md: kernel durations of the
+    decode chains next to the graph's time per node."""
+    import csv
+    line = _bench_line(os.path.join(outdir, "prof_decode.log")) or {}
+    rows = list(csv.DictReader(open(os.path.join(outdir, "prof_decode", "decode_kernel_stats.csv"))))
+    md = ["# row_kernel, decode chains: rocprofv3 kernel statistics", "",
+          "Command (`$REPO` is the repository root):", "", "    " + PROFILE_COMMANDS["trace_decode"], "",
+          "Kernel source sha256[:16]: `%s`" % line.get("kernel_source", "?"), "",
+          "Each chain is captured once in a graph and replayed (5 warm-up + 200 timed "
+          "replays), then the same-length graph of the empty kernel is replayed. Every "
+          "row-kernel instance below belongs to exactly one chain.", "",
+          "| kernel | calls | average µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        md.append("| `%s` | %s | %.2f | %.2f | %.2f | %s |" % (
+            r["Name"].replace("(anonymous namespace)::", ""), r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, r["Percentage"]))
+    ex = line.get("extras", {})
+    fl = [r for r in rows if "floor_kernel" in r["Name"]]
+    if fl:
+        md += ["", "The tracer adds time to every dispatch: the empty kernel itself averages "
+               "%.2f µs here and a graph node of it takes the per-node time below, against "
+               "1.6-1.7 µs untraced. Compare the instances with each other and with the empty "
+               "kernel; bench.py's untraced extras give the per-call times." % (
+                   float(fl[0]["AverageNs"]) / 1e3)]
+    if ex:
+        md += ["", "The same run's graph timings under the tracer (HIP events around each replay):", "",
+               "| chain | µs per call (p50) | empty-kernel µs per node | ratio |", "|---|---|---|---|"]
+        for k, v in ex.items():
+            md.append("| %s | %.2f | %.2f | %.2f |" % (k, v["us_per_call_p50"],
+                                                     v["floor_us_per_node_p50"], v["ratio_to_floor"]))
+    with open(os.path.join(PROFILES, "row_kernel_decode_chains_stats.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
+# ------------------------------------------------------------ extras
+
+def extra_table():
+    """label -> zero-argument callable of every secondary measurement."""
+    t = {"stream_copy_1GiB": stream_copy_gbps,
+         "prefill_n8_t512_d8192": lambda: prefill_gbps(8, 512, 8192, 100, 10),
+         "fp4_n4_t512_d8192": lambda: prefill_gbps(4, 512, 8192, 100, 10, fp4=True, out=False)}
+    for label, out_, kw in [("allreduce_only_n8_t4096_d8192", True, dict(norm=False)),
+                            ("fp8_n8_t4096_d8192", False, dict(fp8=True)),
+                            ("no_residual_n8_t4096_d8192", True, dict(residual=False)),
+                            ("sentinel_reset_n8_t4096_d8192", True, dict(reset=True))]:
+        t[label] = (lambda out_=out_, kw=kw: prefill_gbps(8, 4096, 8192, 30, 5, out=out_, **kw))
+    for (nn, tt, dd, kk, mode, fp4, label) in [
+            (2, 1, 4096, 100, "", False, "decode_n2_t1_d4096_x100"),
+            (8, 8, 4096, 64, "", False, "decode_n8_t8_d4096_chain64"),
+            (4, 8, 8192, 160, "", False, "decode_n4_t8_d8192_chain160"),
+            (8, 8, 8192, 160, "", False, "decode_n8_t8_d8192_chain160"),
+            (4, 8, 8192, 160, "ll", False, "decode_n4_t8_d8192_chain160_ll"),
+            (8, 8, 8192, 160, "ll", False, "decode_n8_t8_d8192_chain160_ll"),
+            (8, 8, 8192, 160, "sentinel", False, "decode_n8_t8_d8192_chain160_sentinel"),
+            (8, 8, 8192, 160, "fp8", False, "decode_n8_t8_d8192_chain160_fp8"),
+            (4, 1, 8192, 100, "", True, "fp4_n4_t1_d8192_x100"),
+            (4, 8, 8192, 100, "", True, "fp4_n4_t8_d8192_x100"),
+            (4, 64, 8192, 100, "", True, "fp4_n4_t64_d8192_x100")]:
+        t[label] = (lambda nn=nn, tt=tt, dd=dd, kk=kk, mode=mode, fp4=fp4:
+                    decode_chain(nn, tt, dd, kk, ll=mode == "ll", fp4=fp4, out=not fp4,
+                                 sentinel=mode == "sentinel", fp8=mode == "fp8"))
+    return t
+
+
+def run_extras(only=None):
+    import torch
+    out = {}
+    for label, fn in extra_table().items():
+        if only and label not in only:
+            continue
+        log("extra %s" % label)
+        out[label] = fn()
+        torch.cuda.empty_cache()
+    return out
 
 
 # ------------------------------------------------------------ main
@@ -460,6 +547,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the streaming-copy reference (counter calibration)")
+    ap.add_argument("--only-extra", action="append", metavar="LABEL",
+                    help="run only these secondary measurements (no timed workload) and "
+                         "print them as one JSON object; repeatable")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 outputs under DIR, then exit")
     args = ap.parse_args(argv)
@@ -484,6 +574,14 @@ def main(argv=None):
         r = stream_copy_gbps()
         print(json.dumps(dict(stream_copy=r)), flush=True)
         return 0
+    if args.only_extra:
+        unknown = set(args.only_extra) - set(extra_table())
+        if unknown:
+            print("unknown extra(s): %s" % ", ".join(sorted(unknown)), file=sys.stderr)
+            return 2
+        print(json.dumps(dict(extras=run_extras(set(args.only_extra)),
+                              kernel_source=source_digest())), flush=True)
+        return 0
 
     name = "prefill_n8_t4096_d8192"
     log("generating %s" % name)
@@ -501,38 +599,7 @@ def main(argv=None):
     del sets
     torch.cuda.empty_cache()
 
-    extras = {}
-    if not args.no_extras:
-        log("stream copy reference")
-        extras["stream_copy_1GiB"] = stream_copy_gbps()
-        log("prefill t=512")
-        extras["prefill_n8_t512_d8192"] = prefill_gbps(8, 512, 8192, 100, 10)
-        log("fp4 t=512")
-        extras["fp4_n4_t512_d8192"] = prefill_gbps(4, 512, 8192, 100, 10, fp4=True, out=False)
-        for label, out_, kw in [("allreduce_only_n8_t4096_d8192", True, dict(norm=False)),
-                                ("fp8_n8_t4096_d8192", False, dict(fp8=True)),
-                                ("no_residual_n8_t4096_d8192", True, dict(residual=False)),
-                                ("sentinel_reset_n8_t4096_d8192", True, dict(reset=True))]:
-            log("pattern %s" % label)
-            extras[label] = prefill_gbps(8, 4096, 8192, 30, 5, out=out_, **kw)
-            torch.cuda.empty_cache()
-        for (nn, tt, dd, kk, ll, fp4, label) in [
-                (2, 1, 4096, 100, False, False, "decode_n2_t1_d4096_x100"),
-                (8, 8, 4096, 64, False, False, "decode_n8_t8_d4096_chain64"),
-                (4, 8, 8192, 160, False, False, "decode_n4_t8_d8192_chain160"),
-                (8, 8, 8192, 160, False, False, "decode_n8_t8_d8192_chain160"),
-                (4, 8, 8192, 160, True, False, "decode_n4_t8_d8192_chain160_ll"),
-                (8, 8, 8192, 160, True, False, "decode_n8_t8_d8192_chain160_ll"),
-                (8, 8, 8192, 160, "sentinel", False, "decode_n8_t8_d8192_chain160_sentinel"),
-                (8, 8, 8192, 160, "fp8", False, "decode_n8_t8_d8192_chain160_fp8"),
-                (4, 1, 8192, 100, False, True, "fp4_n4_t1_d8192_x100"),
-                (4, 8, 8192, 100, False, True, "fp4_n4_t8_d8192_x100"),
-                (4, 64, 8192, 100, False, True, "fp4_n4_t64_d8192_x100")]:
-            log("decode %s" % label)
-            extras[label] = decode_chain(nn, tt, dd, kk, ll=ll is True, fp4=fp4, out=not fp4,
-                                         sentinel=ll == "sentinel", fp8=ll == "fp8")
-            torch.cuda.empty_cache()
-
+    extras = {} if args.no_extras else run_extras()
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
