@@ -105,6 +105,10 @@ uint8_t oracle_e4m3_rne(float x) {
   if (isnan(x)) return 0x7F;
   double ax = (double)x;
   if (ax < 0) ax = -ax;
+  /* 448 is the largest finite code: every larger magnitude (inf included) is
+   * nearer to it than to any other. Decided here because for |x| beyond
+   * about 2^53 the distances below are no longer exact in double. */
+  if (ax > 448.0) return 0x7E;
   uint8_t best = 0;
   double bestd = INFINITY;
   for (int c = 0; c <= 0x7E; ++c) {

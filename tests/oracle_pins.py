@@ -125,6 +125,11 @@ def _e4m3_sweep_points():
         pts += ulp_steps(f32(float(E4M3[i])), 1)
     pts += [f32(448), f32(449), f32(463.9), f32(464), f32(1000), f32(2.0 ** -10),
             f32(2.0 ** -12), f32(0)]
+    # saturation over the whole fp32 range: every power of two above 448, its
+    # neighbours, and the largest finite float
+    for e in range(9, 128):
+        pts += ulp_steps(f32(2.0 ** e), 1)
+    pts += [np.float32(np.finfo(np.float32).max)]
     return np.array([v for v in pts if not np.signbit(v)], np.float32)
 
 

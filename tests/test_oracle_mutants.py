@@ -50,6 +50,7 @@ MUTANTS = {
     "bf16_truncate": [("  if (dlo < dhi)\n    pick = lo;", "  if (1)\n    pick = lo;")],
     "e4m3_ties_down": [(E4M3_TIE, E4M3_TIE.replace(
         "dist < bestd || (dist == bestd && (c & 1) == 0 && (best & 1) == 1)", "dist < bestd"))],
+    "e4m3_no_saturation_guard": [("  if (ax > 448.0) return 0x7E;\n", "")],
     "e4m3_subnormal_exponent": [("ldexp((double)m / 8.0, -6)", "ldexp((double)m / 8.0, -7)")],
     "e2m1_ties_down": [(E2M1_TIE, E2M1_TIE.replace(
         "dist < bestd || (dist == bestd && (c & 1) == 0 && (best & 1) == 1)", "dist < bestd"))],
