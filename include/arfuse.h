@@ -251,6 +251,14 @@ int arfuse_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
  */
 int arfuse_round_bf16(const float* x, int64_t n, uint16_t* out, void* stream);
 
+/*
+ * arfuse_round_fp8 — test entry: the fused kernel's FP8 conversion with
+ * inv_scale 1 (E4M3FN, round to nearest even, sign kept, magnitudes above 448
+ * saturating to 448) applied to x (device fp32 [n], 16-byte aligned), written
+ * to out (device uint8 [n], 4-byte aligned). n a multiple of 4; x finite.
+ */
+int arfuse_round_fp8(const float* x, int64_t n, uint8_t* out, void* stream);
+
 /* Static description of a status code. */
 const char* arfuse_status_string(int status);
 

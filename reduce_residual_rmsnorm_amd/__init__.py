@@ -33,7 +33,7 @@ ARFUSE_MAX_POLLS = 1 << 20
 
 # The exported functions, as declared in include/arfuse.h.
 EXPORTED = ("arfuse_rmsnorm", "arfuse_rmsnorm_ex", "arfuse_quantize_fp4", "arfuse_query_launch",
-            "arfuse_launch_floor", "arfuse_stream_copy", "arfuse_round_bf16",
+            "arfuse_launch_floor", "arfuse_stream_copy", "arfuse_round_bf16", "arfuse_round_fp8",
             "arfuse_status_string", "arfuse_version")
 
 
@@ -93,6 +93,8 @@ def _load(path: str = LIB_PATH):
     lib.arfuse_stream_copy.restype = I
     lib.arfuse_round_bf16.argtypes = [P, I64, P, P]
     lib.arfuse_round_bf16.restype = I
+    lib.arfuse_round_fp8.argtypes = [P, I64, P, P]
+    lib.arfuse_round_fp8.restype = I
     lib.arfuse_status_string.argtypes = [I]
     lib.arfuse_status_string.restype = ctypes.c_char_p
     lib.arfuse_version.argtypes = []
@@ -221,6 +223,12 @@ def arfuse_round_bf16(x, out, stream=None) -> None:
     """Test entry: the kernel's fp32 -> bf16 rounding of x into out."""
     rc = lib.arfuse_round_bf16(_addr(x), int(x.numel()), _addr(out), _stream(stream))
     _check(rc, "arfuse_round_bf16")
+
+
+def arfuse_round_fp8(x, out, stream=None) -> None:
+    """Test entry: the kernel's FP8 conversion (inv_scale 1) of x into out."""
+    rc = lib.arfuse_round_fp8(_addr(x), int(x.numel()), _addr(out), _stream(stream))
+    _check(rc, "arfuse_round_fp8")
 
 
 def arfuse_status_string(code: int) -> str:

@@ -66,6 +66,18 @@ __global__ __launch_bounds__(256) void round_bf16_kernel(const f32x2* x, int64_t
   if (i < npairs) out[i] = pack_bf16(x[i].x, x[i].y);
 }
 
+// The FP8 conversion of the fused kernel (inv_scale 1) applied to an fp32
+// array (test entry).
+__global__ __launch_bounds__(256) void round_fp8_kernel(const f32x4* x, int64_t nquads,
+                                                        uint32_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nquads) {
+    const f32x4 v = x[i];
+    const float y[4] = {v.x, v.y, v.z, v.w};
+    out[i] = fp8_quad(y, 1.0f);
+  }
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* src, u32x4* dst, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) store16(dst + i, load16<true>(src + i));
@@ -375,6 +387,23 @@ int arfuse_round_bf16(const float* x, int64_t n, uint16_t* out, void* stream) {
   int64_t np = npairs;
   void* args[] = {&xx, &np, &oo};
   hipError_t e = hipLaunchKernel((const void*)round_bf16_kernel, dim3((unsigned)grid), dim3(256),
+                                 args, 0, (hipStream_t)stream);
+  return launch_status(e);
+}
+
+int arfuse_round_fp8(const float* x, int64_t n, uint8_t* out, void* stream) {
+  if (n < 0 || n % 4) return ARFUSE_ERR_INVALID_ARG;
+  if (n == 0) return ARFUSE_OK;
+  if (!x || !out || !aligned16(x) || ((uintptr_t)out & 3u)) return ARFUSE_ERR_INVALID_ARG;
+  if (overlap(range_of(x, n * 4), range_of(out, n))) return ARFUSE_ERR_INVALID_ARG;
+  const int64_t nquads = n / 4;
+  const int64_t grid = (nquads + 255) / 256;
+  if (grid > 0x7FFFFFFFLL) return ARFUSE_ERR_UNSUPPORTED;
+  const f32x4* xx = (const f32x4*)x;
+  uint32_t* oo = (uint32_t*)out;
+  int64_t nq = nquads;
+  void* args[] = {&xx, &nq, &oo};
+  hipError_t e = hipLaunchKernel((const void*)round_fp8_kernel, dim3((unsigned)grid), dim3(256),
                                  args, 0, (hipStream_t)stream);
   return launch_status(e);
 }

@@ -304,11 +304,17 @@ __device__ __forceinline__ void fp4_quad(const float* y, uint32_t& codes4, uint3
   scale = sc;
 }
 
-// FP8 E4M3 code of y * inv_scale: sign bit 7, magnitude by e4m3_rne
-// (nearest, ties to even, saturating at 448).
-__device__ __forceinline__ uint32_t fp8_code(float y, float inv_scale) {
-  const float q = y * inv_scale;
-  return ((__float_as_uint(q) >> 31) << 7) | e4m3_rne(fabsf(q));
+// FP8 E4M3 codes of four values times inv_scale, packed little-endian into a
+// dword: gfx950's OCP E4M3 conversion (round to nearest even, sign kept) on
+// q = fl32(y * inv_scale) clamped to [-448, 448] first, so magnitudes above
+// 448 saturate to 448 instead of becoming NaN.
+__device__ __forceinline__ uint32_t fp8_quad(const float* y, float inv_scale) {
+  float q[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) q[e] = __builtin_amdgcn_fmed3f(y[e] * inv_scale, -448.0f, 448.0f);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], r, true);
+  return (uint32_t)r;
 }
 
 // Typed access at a byte offset from a base pointer. Row base pointers are
@@ -590,12 +596,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
       }
     }
     if constexpr (FP8) {
-      uint32_t q[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        q[j] = fp8_code(y[4 * j], a.fp8_inv_scale) | (fp8_code(y[4 * j + 1], a.fp8_inv_scale) << 8) |
-               (fp8_code(y[4 * j + 2], a.fp8_inv_scale) << 16) |
-               (fp8_code(y[4 * j + 3], a.fp8_inv_scale) << 24);
+      const uint32_t q[2] = {fp8_quad(y, a.fp8_inv_scale), fp8_quad(y + 4, a.fp8_inv_scale)};
       if constexpr (LL) {
         if (ok[k][0]) __builtin_nontemporal_store(q[0], at_w<uint32_t>(frow, eo[k][0]));
         if (ok[k][1]) __builtin_nontemporal_store(q[1], at_w<uint32_t>(frow, eo[k][1]));

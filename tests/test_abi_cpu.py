@@ -187,6 +187,19 @@ def test_query_launch_auto(d, block, vpt):
     assert info.block * info.vpt * 8 >= d
 
 
+@pytest.mark.parametrize("n,t,d,extra", [(8, 8, 8192, 8 * 8), (3, 5, 1040, 3 * 4), (2, 128, 4096, 2 * 128),
+                                         (3, 129, 1040, 0), (8, 4096, 8192, 0)])
+def test_query_launch_sentinel_reset_blocks(n, t, d, extra):
+    """Up to 128 rows, n * ceil(t*d/8 / block) reset workgroups follow the rows."""
+    S = arf.ARFUSE_LAYOUT_SENTINEL
+    info = arf.arfuse_query_launch(n, t, d, layout=S, reset=[spaced(i) for i in range(n)])
+    base = arf.arfuse_query_launch(n, t, d, layout=S)
+    assert base.grid == t
+    assert info.grid == t + extra
+    if extra:
+        assert extra == n * -(-(t * d // 8) // info.block)
+
+
 def test_query_launch_override():
     info = arf.arfuse_query_launch(8, 3, 8192, block_threads=512)
     assert (info.block, info.vpt) == (512, 2)
@@ -206,6 +219,13 @@ def test_quantize_and_copy_validation():
     assert c(spaced(0), spaced(1), 24, 0) == arf.ARFUSE_ERR_INVALID_ARG
     assert c(spaced(0), spaced(0) + 16, 64, 0) == arf.ARFUSE_ERR_INVALID_ARG
     assert c(spaced(0), spaced(1), 0, 0) == arf.ARFUSE_OK
+    for r, vec in ((arf.lib.arfuse_round_bf16, 2), (arf.lib.arfuse_round_fp8, 4)):
+        assert r(spaced(0), vec + 1, spaced(1), 0) == arf.ARFUSE_ERR_INVALID_ARG   # not a multiple
+        assert r(spaced(0), -vec, spaced(1), 0) == arf.ARFUSE_ERR_INVALID_ARG
+        assert r(0, vec, spaced(1), 0) == arf.ARFUSE_ERR_INVALID_ARG
+        assert r(spaced(0), 4 * vec, spaced(0) + 4, 0) == arf.ARFUSE_ERR_INVALID_ARG  # overlap
+        assert r(spaced(0), 0, 0, 0) == arf.ARFUSE_OK
+    assert arf.lib.arfuse_round_fp8(spaced(0) + 8, 4, spaced(1), 0) == arf.ARFUSE_ERR_INVALID_ARG
 
 
 def test_single_hip_runtime_in_process():

@@ -215,6 +215,32 @@ def test_quantize_ragged_rows():
         assert np.array_equal(s, ws) and np.array_equal(c, wc)
 
 
+def test_kernel_fp8_conversion_on_every_tie_pattern():
+    """The fused kernel's FP8 conversion (gfx950's E4M3 convert after a clamp
+    to +-448) equals the oracle's sign | E4M3 round-to-nearest-even with
+    saturation, on every 16-bit prefix combined with each tie and near-tie low
+    half (E4M3 ties and their neighbours all fall on these patterns), and on
+    random patterns."""
+    orc = __import__("oracle").default()
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    pats = (hi[:, None] | lows[None, :]).reshape(-1)
+    rnd = np.random.default_rng(15).integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    x = np.concatenate([pats, rnd]).view(np.float32)
+    x = x[np.isfinite(x)]
+    x = x[: x.size // 4 * 4]
+    want = orc.e4m3_rne(np.abs(x)) | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    xd = dev_f32(x)
+    out = torch.empty(x.size, dtype=torch.uint8, device="cuda:0")
+    note("fp8 conversion sweep n=%d" % x.size)
+    arf.arfuse_round_fp8(xd, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, "fp8 conversion differs at %s: got %s want %s" % (
+        x[bad[:4]].view(np.uint32), got[bad[:4]], want[bad[:4]])
+
+
 def test_kernel_bf16_rounding_on_every_tie_pattern():
     """The fused kernel's fp32 -> bf16 conversion (gfx950's packed convert)
     equals the oracle's round-to-nearest-even on every 16-bit prefix combined

@@ -166,15 +166,19 @@ def test_sentinel_pending_vectors_reported(sentinel, max_polls):
     assert_y_close(got["out"][clean], ref["y32"][clean])
 
 
-def test_sentinel_reset_refills_slots():
-    ci = si.make_call(3, 5, 1040, seed=81)
-    t, d = ci.t, ci.d
+# t <= 128: extra workgroups of the launch write the reset; above, every row
+# workgroup refills its own row at its end.
+@pytest.mark.parametrize("n,t,d", [(3, 5, 1040), (2, 128, 4096), (3, 129, 1040), (8, 300, 8192)])
+def test_sentinel_reset_refills_slots(n, t, d):
+    ci = si.make_call(n, t, d, seed=81)
+    info = arf.arfuse_query_launch(n, t, d, layout=SENT, reset=[1 << 32] * n)
+    note("sentinel reset n=%d t=%d d=%d grid=%d" % (n, t, d, info.grid))
     parts = [dev_u16(p) for p in ci.partials]
     res = dev_u16(ci.residual)
     g = dev_f32(ci.gamma)
     o = torch.empty((t, d), dtype=torch.bfloat16, device=DEV)
     ro = torch.empty_like(o)
-    slots = [torch.full((t, d), 7, dtype=torch.int16, device=DEV) for _ in range(3)]
+    slots = [torch.full((t, d), 7, dtype=torch.int16, device=DEV) for _ in range(n)]
     note("sentinel reset")
     arf.arfuse_rmsnorm_ex(parts, res, g, float(ci.eps), o, ro, layout=SENT, sentinel=0xFFC1,
                           reset=slots)
