@@ -207,12 +207,14 @@ def time_graph(g, reps: int):
 
 def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = False,
                  out: bool = True, reps: int = 200, seed: int = 0, fp8: bool = False,
-                 sentinel: bool = False):
+                 sentinel: bool = False, fresh=None):
     """µs per call of a k-call chain captured in one graph (call c reads call
     c-1's residual_out), and of the same-length graph of the empty kernel
     with the same launch (the per-node floor). `sentinel` reads the slots in
     the sentinel layout and refills a second slot set on every call (the
-    triple-buffer reset), `fp8` adds the FP8 output."""
+    triple-buffer reset), `fp8` adds the FP8 output. `fresh` (default: LL
+    only) gives every call its own partial buffers, as a peer's push would,
+    instead of re-reading one set that stays in the caches."""
     import numpy as np
     import torch
 
@@ -220,15 +222,16 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
     import seeded_inputs as si
 
     ci = si.make_call(n, t, d, seed=seed, outlier_frac=0.001 if fp4 else 0.0)
-    flags = [ci.ll_base + c for c in range(k)]
+    fresh = ll if fresh is None else fresh
+    # per call: its own flag (LL, fresh) or one flag for the reused set
+    flags = [ci.ll_base + (c if fresh else 0) for c in range(k)]
+    nsets = k if fresh else 1
     if ll:
-        # each call reads its own LL buffers carrying its own step flag
-        packed = np.stack([si.ll_pack_all(ci.partials, f) for f in flags])
+        packed = np.stack([si.ll_pack_all(ci.partials, flags[c]) for c in range(nsets)])
         pdev = dev_bytes(packed)
-        parts = [[pdev[c, i] for i in range(n)] for c in range(k)]
     else:
-        p = [dev_bf16(x) for x in ci.partials]
-        parts = [p] * k
+        pdev = dev_bf16(np.stack([ci.partials] * nsets))
+    parts = [[pdev[c % nsets, i] for i in range(n)] for c in range(k)]
     res0 = dev_bf16(ci.residual)
     bufs = [torch.empty_like(res0), torch.empty_like(res0)]
     gamma = torch.from_numpy(ci.gamma).to(_dev())
@@ -278,7 +281,7 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
         raise RuntimeError("arrival reported bad during the benchmark: %s" % st)
     info = arf.arfuse_query_launch(n, t, d, epi)
     r = dict(n=n, t=t, d=d, calls=k, layout="ll" if ll else "sentinel" if sentinel else "plain",
-             fp4=fp4, fp8=fp8, reset=sentinel,
+             fp4=fp4, fp8=fp8, reset=sentinel, fresh_partials=bool(fresh),
              grid=int(info.grid), block=int(info.block),
              us_per_call_p50=chain["p50"] / k, chain_us_p50=chain["p50"],
              chain_us_p10=chain["p10"], chain_us_p90=chain["p90"],
@@ -514,13 +517,18 @@ def extra_table():
             (4, 8, 8192, 160, "ll", False, "decode_n4_t8_d8192_chain160_ll"),
             (8, 8, 8192, 160, "ll", False, "decode_n8_t8_d8192_chain160_ll"),
             (8, 8, 8192, 160, "sentinel", False, "decode_n8_t8_d8192_chain160_sentinel"),
+            (8, 8, 8192, 160, "fresh", False, "decode_n8_t8_d8192_chain160_fresh"),
+            (8, 8, 8192, 160, "ll_reused", False, "decode_n8_t8_d8192_chain160_ll_reused"),
+            (8, 8, 8192, 160, "sentinel_fresh", False, "decode_n8_t8_d8192_chain160_sentinel_fresh"),
             (8, 8, 8192, 160, "fp8", False, "decode_n8_t8_d8192_chain160_fp8"),
             (4, 1, 8192, 100, "", True, "fp4_n4_t1_d8192_x100"),
             (4, 8, 8192, 100, "", True, "fp4_n4_t8_d8192_x100"),
             (4, 64, 8192, 100, "", True, "fp4_n4_t64_d8192_x100")]:
         t[label] = (lambda nn=nn, tt=tt, dd=dd, kk=kk, mode=mode, fp4=fp4:
-                    decode_chain(nn, tt, dd, kk, ll=mode == "ll", fp4=fp4, out=not fp4,
-                                 sentinel=mode == "sentinel", fp8=mode == "fp8"))
+                    decode_chain(nn, tt, dd, kk, ll=mode.startswith("ll"), fp4=fp4, out=not fp4,
+                                 sentinel=mode.startswith("sentinel"), fp8=mode == "fp8",
+                                 fresh=(True if "fresh" in mode else False if "reused" in mode
+                                        else None)))
     return t
 
 
