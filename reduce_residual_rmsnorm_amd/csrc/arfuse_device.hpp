@@ -146,14 +146,22 @@ __device__ __forceinline__ uint32_t e2m1_rne(float a, const E2M1Thresholds& th) 
   return (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (a > tl ? 1u : 0u);
 }
 
+// Value of lane (lane XOR 1) for CTRL = 0xB1 (quad_perm [1,0,3,2]), of lane
+// (lane XOR 2) for CTRL = 0x4E (quad_perm [2,3,0,1]): a DPP move, a plain
+// vector instruction (a wave shuffle would go through the LDS unit).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 // FP4 of the 8 values a lane holds. Lanes (2m, 2m+1) hold one 16-element
-// block, so the block max is one XOR-1 shuffle away. Every lane of the wave
-// must call this (the shuffle is a wave-wide operation).
+// block, so the block max is one lane swap (lane XOR 1) away. Every lane of the
+// wave must call this (the swap reads the partner lane's register).
 __device__ __forceinline__ void fp4_pair(const float y[8], uint32_t& codes8, uint32_t& scale) {
   float am = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(y[e]));
-  am = fmaxf(am, __shfl_xor(am, 1));
+  am = fmaxf(am, dpp_f32<0xB1>(am));
   const uint32_t sc = e4m3_rne(am / 6.0f);
   const E2M1Thresholds th = e2m1_thresholds(e4m3_value(sc));
   uint32_t c = 0;
@@ -289,11 +297,11 @@ __device__ __forceinline__ u32x2 load8(const u32x2* p) {
 __device__ __forceinline__ void store8(u32x2* p, u32x2 v) { __builtin_nontemporal_store(v, p); }
 
 // FP4 of a 4-element group in the LL geometry: lanes 4m..4m+3 hold one
-// 16-element block (two XOR shuffles give its max); 4 codes = 16 bits.
+// 16-element block (two lane swaps give its max); 4 codes = 16 bits.
 __device__ __forceinline__ void fp4_quad(const float* y, uint32_t& codes4, uint32_t& scale) {
   float am = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
-  am = fmaxf(am, __shfl_xor(am, 1));
-  am = fmaxf(am, __shfl_xor(am, 2));
+  am = fmaxf(am, dpp_f32<0xB1>(am));
+  am = fmaxf(am, dpp_f32<0x4E>(am));
   const uint32_t sc = e4m3_rne(am / 6.0f);
   const E2M1Thresholds th = e2m1_thresholds(e4m3_value(sc));
   uint32_t c = 0;
