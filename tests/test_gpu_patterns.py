@@ -96,7 +96,7 @@ PATTERNS = {
 }
 
 
-@pytest.mark.parametrize("layout", [0, LL])
+@pytest.mark.parametrize("layout", [0, LL, SENT])
 @pytest.mark.parametrize("pattern", sorted(PATTERNS))
 def test_pattern(pattern, layout):
     kw = PATTERNS[pattern]
@@ -107,7 +107,10 @@ def test_pattern(pattern, layout):
                       out=kw.get("out", True), fp4=kw.get("fp4", False),
                       fp8_inv_scale=kw.get("fp8"), residual_out=kw.get("rout", True))
     note("pattern %s layout %d" % (pattern, layout))
-    got = run(ci, layout=layout, flag=flag, **kw)
+    extra = dict(status=new_status(), max_polls=1) if layout == SENT else {}
+    got = run(ci, layout=layout, flag=flag, **kw, **extra)
+    if extra:
+        assert read_status(extra["status"]) == (0, 0)
     if kw.get("rout", True):
         assert_residual_exact(got["residual_out"], ref["residual_out"])
     if got["out"] is not None:
@@ -186,6 +189,25 @@ def test_sentinel_reset_refills_slots(n, t, d):
     for sl in slots:
         assert np.all(sl.cpu().numpy().view(np.uint16) == 0xFFC1)
     ref = orc().allreduce_rmsnorm(ci.partials, ci.residual, ci.gamma, ci.eps)
+    assert_residual_exact(host_u16(ro), ref["residual_out"])
+
+
+@pytest.mark.parametrize("t", [9, 130])
+def test_sentinel_allreduce_only_with_reset(t):
+    """All-reduce only (no gamma) returns before the norm; the row workgroups'
+    reset (t > 128) or the extra reset workgroups (t <= 128) must still run."""
+    n, d = 4, 4096
+    ci = si.make_call(n, t, d, seed=84)
+    parts = [dev_u16(p) for p in ci.partials]
+    ro = torch.empty((t, d), dtype=torch.bfloat16, device=DEV)
+    slots = [torch.zeros((t, d), dtype=torch.int16, device=DEV) for _ in range(n)]
+    note("sentinel all-reduce only with reset t=%d" % t)
+    arf.arfuse_rmsnorm_ex(parts, dev_u16(ci.residual), None, float(ci.eps), None, ro, t=t, d=d,
+                          layout=SENT, reset=slots)
+    torch.cuda.synchronize()
+    for sl in slots:
+        assert np.all(sl.cpu().numpy().view(np.uint16) == arf.ARFUSE_SENTINEL_DEFAULT)
+    ref = orc().fused(ci.partials, ci.residual, None, ci.eps)
     assert_residual_exact(host_u16(ro), ref["residual_out"])
 
 
