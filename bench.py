@@ -503,7 +503,10 @@ def extra_table():
     """label -> zero-argument callable of every secondary measurement."""
     t = {"stream_copy_1GiB": stream_copy_gbps,
          "prefill_n8_t512_d8192": lambda: prefill_gbps(8, 512, 8192, 100, 10),
-         "fp4_n4_t512_d8192": lambda: prefill_gbps(4, 512, 8192, 100, 10, fp4=True, out=False)}
+         "fp4_n4_t512_d8192": lambda: prefill_gbps(4, 512, 8192, 100, 10, fp4=True, out=False),
+         # wide rows (the kernel's chunk pipeline), same bytes as the timed workload
+         "prefill_n8_t1024_d32768": lambda: prefill_gbps(8, 1024, 32768, 30, 5),
+         "prefill_n8_t512_d65536": lambda: prefill_gbps(8, 512, 65536, 30, 5)}
     for label, out_, kw in [("allreduce_only_n8_t4096_d8192", True, dict(norm=False)),
                             ("fp8_n8_t4096_d8192", False, dict(fp8=True)),
                             ("no_residual_n8_t4096_d8192", True, dict(residual=False)),

@@ -180,14 +180,30 @@ __device__ __forceinline__ bool ll_ok(u32x4 w, uint64_t flag) {
   return (w.z == (uint32_t)flag) & (w.w == (uint32_t)(flag >> 32));
 }
 
-// A word whose flag does not match is re-read with cache-bypassing (volatile)
-// loads, a short sleep apart, at most max_polls times. Returns the last word
-// read; *bad counts a word that never matched.
-__device__ __forceinline__ u32x4 ll_repoll(const u32x4* p, u32x4 w, uint64_t flag,
-                                                     uint32_t max_polls, uint32_t* bad) {
+// Re-read of a 16-byte vector another agent may still be writing: a buffer
+// load through a descriptor of the row (scalar registers) at the lane's
+// 32-bit offset, bypassing the caches (sc0 sc1) and kept in the polling loop
+// (the compiler's volatile bit, 1 << 31). A pointer-based volatile load would
+// need a 64-bit address per partial in vector registers, and the compiler
+// keeps all of them live through the row. Word 3 of the descriptor: raw
+// 32-bit data format, as gfx9-family buffer resources take it.
+constexpr int kRereadPolicy = (int)0x80000011u;
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ u32x4 reread16(const char* row, uint32_t row_bytes, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, (int)row_bytes, kBufferWord3);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kRereadPolicy);
+}
+
+// A word whose flag does not match is re-read, a short sleep apart, at most
+// max_polls times. Returns the last word read; *bad counts a word that never
+// matched.
+__device__ __forceinline__ u32x4 ll_repoll(const char* row, uint32_t row_bytes, uint32_t off,
+                                           u32x4 w, uint64_t flag, uint32_t max_polls,
+                                           uint32_t* bad) {
   for (uint32_t i = 0; i < max_polls; ++i) {
     __builtin_amdgcn_s_sleep(2);
-    w = *(const volatile u32x4*)p;
+    w = reread16(row, row_bytes, off);
     if (ll_ok(w, flag)) return w;
   }
   *bad += 1;
@@ -204,8 +220,8 @@ __device__ __forceinline__ bool holds_sentinel(u32x4 w, uint32_t s2) {
          ((w.w & 0xFFFFu) == lo) | ((w.w & 0xFFFF0000u) == hi);
 }
 
-// Sentinel layout, patterns that are not NaN: nonzero iff some 16-bit half of
-// the vector equals the pattern. Per dword t = w ^ s2, a half of t is zero
+// Sentinel layout: nonzero iff some 16-bit half of the vector equals the
+// pattern. Per dword t = w ^ s2, a half of t is zero
 // iff (t - 0x00010001) & ~t has that half's top bit set; a borrow out of a
 // zero low half can only flag the high half when the low one already is.
 __device__ __forceinline__ uint32_t zero_half4(u32x4 w, uint32_t s2) {
@@ -215,11 +231,12 @@ __device__ __forceinline__ uint32_t zero_half4(u32x4 w, uint32_t s2) {
 }
 
 // Re-read a vector that still holds the sentinel, bounded like ll_repoll.
-__device__ __forceinline__ u32x4 sentinel_repoll(const u32x4* p, u32x4 w, uint32_t s2,
+__device__ __forceinline__ u32x4 sentinel_repoll(const char* row, uint32_t row_bytes,
+                                                 uint32_t off, u32x4 w, uint32_t s2,
                                                  uint32_t max_polls, uint32_t* bad) {
   for (uint32_t i = 0; i < max_polls; ++i) {
     __builtin_amdgcn_s_sleep(2);
-    w = *(const volatile u32x4*)p;
+    w = reread16(row, row_bytes, off);
     if (!holds_sentinel(w, s2)) return w;
   }
   *bad += 1;
@@ -340,12 +357,34 @@ __device__ __forceinline__ T* at_w(char* base, uint32_t off) {
   return reinterpret_cast<T*>(base + off);
 }
 
+// Pipeline depth of a row kernel instance: how many chunks' loads may be in
+// flight while a chunk is processed. A chunk is N partial loads (two words
+// each for LL) plus the residual, 4 VGPRs per 16 bytes; h keeps 8 floats per
+// chunk for the whole row. All chunks at once (D = VPT) while that fits the
+// 128 VGPRs of a 1024-thread block with room to spare, else two, else one.
+template <int N, int VPT, bool LL>
+constexpr int pipeline_depth() {
+  constexpr int chunk = 4 * N * (LL ? 2 : 1) + 4;
+  constexpr int fixed = 8 * VPT + 28;
+  if (VPT * chunk + 8 * VPT + fixed <= 112) return VPT;  // gamma preloaded too
+  if (2 * chunk + fixed <= 112) return 2 < VPT ? 2 : VPT;
+  return 1;
+}
+
 template <int N, int VPT, bool LL, bool SENT, int EPI>
 __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   constexpr bool NORM = EPI != 0;
   constexpr bool OUT = (EPI & ARFUSE_EPI_BF16) != 0;
   constexpr bool FP4 = (EPI & ARFUSE_EPI_FP4) != 0;
   constexpr bool FP8 = (EPI & ARFUSE_EPI_FP8) != 0;
+  constexpr int D = pipeline_depth<N, VPT, LL>();
+  constexpr bool ALL_AT_ONCE = D == VPT;
+  constexpr int W = LL ? 2 : 1;  // 16-byte loads per partial per chunk
+  // gamma: with the partials' loads when everything fits at once (not in
+  // the sentinel layout, where it follows the arrival check so the re-poll
+  // path's registers stay free); otherwise per chunk in the output loop
+  constexpr bool G_EARLY = NORM && ALL_AT_ONCE && !SENT;
+  constexpr bool G_AFTER_ARRIVAL = NORM && ALL_AT_ONCE && SENT;
   const int lane = threadIdx.x;
   const int nthr = blockDim.x;
   if constexpr (SENT) {
@@ -382,29 +421,47 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   // load stays in bounds; idle lanes store nothing and add nothing
   uint32_t eo[VPT][2];
   bool ok[VPT][2];
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) {
+  auto set_offsets = [&](int k, int ln) {
     if constexpr (LL) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint32_t e = (uint32_t)group_elem<LL>(k, j, lane, nthr);
+        const uint32_t e = (uint32_t)group_elem<LL>(k, j, ln, nthr);
         ok[k][j] = e < d;
         eo[k][j] = ok[k][j] ? e : d - 4;
       }
     } else {  // the two groups of a plain vector share one validity
-      const uint32_t e = (uint32_t)group_elem<LL>(k, 0, lane, nthr);
+      const uint32_t e = (uint32_t)group_elem<LL>(k, 0, ln, nthr);
       ok[k][0] = ok[k][1] = e < d;
       eo[k][0] = ok[k][0] ? e : d - 8;
       eo[k][1] = eo[k][0] + 4;
     }
-  }
+  };
+  // Wide rows recompute the offsets in each phase from a copy of the lane
+  // index the compiler cannot see through, so one phase's offsets do not stay
+  // live (in registers) through the next.
+  auto fresh_offsets = [&]() {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) set_offsets(k, ln);
+  };
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) set_offsets(k, lane);
 
-  // ---- issue every load of the row
-  u32x4 raw[VPT][N][LL ? 2 : 1];
+  u32x4 raw[VPT][N][W];
   u32x4 rres[VPT];
   f32x4 g[VPT][2];
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) {
+  float h[VPT][8];
+  uint32_t bad = 0;
+
+  // ---- per-chunk steps. The lambdas that load take the row bases by value:
+  // captured by reference, the loads lose the scalar-base + 32-bit-offset
+  // form and each gets a 64-bit address in vector registers.
+  auto load_gamma = [&, grow](int k) {
+    g[k][0] = *at<f32x4>(grow, eo[k][0] * 4);
+    g[k][1] = *at<f32x4>(grow, eo[k][1] * 4);
+  };
+  auto load_chunk = [&, prow, rrow](int k) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       if constexpr (LL) {
@@ -424,27 +481,18 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
         rres[k] = load16<true>(at<u32x4>(rrow, eo[k][0] * 2));
       }
     }
-    if constexpr (NORM && !SENT) {  // sentinel layout: after the arrival check
-      g[k][0] = *at<f32x4>(grow, eo[k][0] * 4);
-      g[k][1] = *at<f32x4>(grow, eo[k][1] * 4);
-    }
-  }
-  // keep the scheduler from interleaving arithmetic into the load block: all
-  // of the row's loads are in flight before the first use
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- arrival. LL: one pass of flag compares. Sentinel: a cheap filter
-  // first; only a lane that holds a word or vector that has not arrived runs
-  // the exact check and the bounded re-poll.
-  uint32_t bad = 0;
-  if constexpr (LL) {
-    // filter: OR of (flag XOR expected) over the lane's words, in vector
-    // integer ops (per-word compares would each make a lane mask for the
-    // scalar unit to combine)
-    const uint32_t flo = (uint32_t)a.ll_flag, fhi = (uint32_t)(a.ll_flag >> 32);
-    uint32_t mis = 0;
-#pragma unroll
-    for (int k = 0; k < VPT; ++k)
+    if constexpr (G_EARLY) load_gamma(k);
+  };
+  // Arrival of chunk k. LL: the filter is the OR of (flag XOR expected) over
+  // the lane's words; sentinel: a zero 16-bit half in (data XOR pattern),
+  // over whole dwords. Both are vector integer ops: per-word or per-element
+  // compares would each make a lane mask for the scalar unit to combine, a
+  // long serial chain. Only a lane the filter flags runs the exact check and
+  // the bounded re-poll.
+  auto arrive = [&, prow](int k) {
+    if constexpr (LL) {
+      const uint32_t flo = (uint32_t)a.ll_flag, fhi = (uint32_t)(a.ll_flag >> 32);
+      uint32_t mis = 0;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         uint32_t m = 0;
@@ -452,104 +500,59 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
         for (int i = 0; i < N; ++i) m |= (raw[k][i][j].z ^ flo) | (raw[k][i][j].w ^ fhi);
         mis |= ok[k][j] ? m : 0u;
       }
-    if (__builtin_expect(mis != 0, 0)) {
-#pragma unroll
-      for (int k = 0; k < VPT; ++k)
+      if (__builtin_expect(mis != 0, 0)) {
 #pragma unroll
         for (int i = 0; i < N; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             if (ok[k][j] && !ll_ok(raw[k][i][j], a.ll_flag))
-              raw[k][i][j] = ll_repoll(at<u32x4>(prow[i], eo[k][j] * 4), raw[k][i][j], a.ll_flag,
+              raw[k][i][j] = ll_repoll(prow[i], d * 4, eo[k][j] * 4, raw[k][i][j], a.ll_flag,
                                        a.max_polls, &bad);
-    }
-  }
-  // exact sentinel check of every vector the lane owns, re-reading the
-  // pending ones (bounded)
-  auto sentinel_wait = [&]() {
+      }
+    } else if constexpr (SENT) {
+      uint32_t z = 0;
 #pragma unroll
-    for (int k = 0; k < VPT; ++k)
+      for (int i = 0; i < N; ++i) z |= zero_half4(raw[k][i][0], a.sentinel2);
+      z = ok[k][0] ? z : 0u;
+      if (__builtin_expect(z != 0, 0)) {
 #pragma unroll
-      for (int i = 0; i < N; ++i)
-        if (ok[k][0] && holds_sentinel(raw[k][i][0], a.sentinel2))
-          raw[k][i][0] = sentinel_repoll(at<u32x4>(prow[i], eo[k][0] * 2), raw[k][i][0],
-                                         a.sentinel2, a.max_polls, &bad);
-  };
-  // refill this row of the slot set a later call reuses; done last, when the
-  // row's data no longer occupy registers
-  auto reset_row = [&]() {
-    if constexpr (SENT) {
-      if (a.flags & kReset) {
-        const u32x4 sv = {a.sentinel2, a.sentinel2, a.sentinel2, a.sentinel2};
-#pragma unroll
-        for (int k = 0; k < VPT; ++k)
-          if (ok[k][0]) {
-#pragma unroll
-            for (int i = 0; i < N; ++i)
-              store16(at_w<u32x4>((char*)a.reset[i] + rb * 2, eo[k][0] * 2), sv);
-          }
+        for (int i = 0; i < N; ++i)
+          if (ok[k][0] && holds_sentinel(raw[k][i][0], a.sentinel2))
+            raw[k][i][0] = sentinel_repoll(prow[i], d * 2, eo[k][0] * 2, raw[k][i][0],
+                                           a.sentinel2, a.max_polls, &bad);
       }
     }
   };
-  if constexpr (SENT) {
-    // The filter: a zero 16-bit half in (data XOR pattern), found with
-    // integer ops on whole dwords. (Per-element compares each write a lane
-    // mask that the scalar unit then has to combine, a long serial chain.)
-    uint32_t z = 0;
+  // rank-ordered fp32 sum of chunk k, residual last
+  auto rank_sum = [&](int k) {
+    u32x4 pv[N];
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      uint32_t zk = 0;
-#pragma unroll
-      for (int i = 0; i < N; ++i) zk |= zero_half4(raw[k][i][0], a.sentinel2);
-      z |= ok[k][0] ? zk : 0u;
+    for (int i = 0; i < N; ++i) {
+      if constexpr (LL)
+        pv[i] = u32x4{raw[k][i][0].x, raw[k][i][0].y, raw[k][i][1].x, raw[k][i][1].y};
+      else
+        pv[i] = raw[k][i][0];
     }
-    if (__builtin_expect(z != 0, 0)) sentinel_wait();
-    if constexpr (NORM) {  // gamma is L2-resident; loading it here keeps the
-                           // re-poll path's registers free
+    float acc[8], f[8];
+    widen8(pv[0], acc);
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        g[k][0] = *at<f32x4>(grow, eo[k][0] * 4);
-        g[k][1] = *at<f32x4>(grow, eo[k][1] * 4);
-      }
+    for (int i = 1; i < N; ++i) {
+      widen8(pv[i], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] + f[e];
     }
-  }
-
-  // ---- rank-ordered fp32 sum, residual last
-  float h[VPT][8];
-  auto rank_sum = [&]() {
+    if (has_res) {
+      widen8(rres[k], f);
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      u32x4 pv[N];
+      for (int e = 0; e < 8; ++e) h[k][e] = acc[e] + f[e];
+    } else {
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        if constexpr (LL)
-          pv[i] = u32x4{raw[k][i][0].x, raw[k][i][0].y, raw[k][i][1].x, raw[k][i][1].y};
-        else
-          pv[i] = raw[k][i][0];
-      }
-      float acc[8], f[8];
-      widen8(pv[0], acc);
-#pragma unroll
-      for (int i = 1; i < N; ++i) {
-        widen8(pv[i], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + f[e];
-      }
-      if (has_res) {
-        widen8(rres[k], f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[k][e] = acc[e] + f[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[k][e] = acc[e];
-      }
+      for (int e = 0; e < 8; ++e) h[k][e] = acc[e];
     }
   };
-  rank_sum();
-  // ---- residual_out, sum of squares
   double ss = 0.0;
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) {
+  // residual_out of chunk k, and its share of the sum of squares
+  auto emit_residual = [&](int k) {
     if (has_rout) {
       const u32x4 hb = narrow8(h[k]);
       if constexpr (LL) {
@@ -563,6 +566,57 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (ok[k][e / 4]) ss += (double)h[k][e] * (double)h[k][e];
+    }
+  };
+  // refill this row of the slot set a later call reuses; done last, when the
+  // row's data no longer occupy registers
+  auto reset_row = [&]() {
+    if constexpr (SENT) {
+      if (a.flags & kReset) {
+        if constexpr (!ALL_AT_ONCE) fresh_offsets();
+        const u32x4 sv = {a.sentinel2, a.sentinel2, a.sentinel2, a.sentinel2};
+#pragma unroll
+        for (int k = 0; k < VPT; ++k)
+          if (ok[k][0]) {
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+              store16(at_w<u32x4>((char*)a.reset[i] + rb * 2, eo[k][0] * 2), sv);
+          }
+      }
+    }
+  };
+
+  // ---- the row's chunks
+  if constexpr (ALL_AT_ONCE) {
+    // every load of the row in flight before the first use; the scheduling
+    // barrier keeps arithmetic out of the load block
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) load_chunk(k);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) arrive(k);
+    if constexpr (G_AFTER_ARRIVAL) {
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) load_gamma(k);
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) rank_sum(k);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) emit_residual(k);
+  } else {
+    // wide rows: loads run D chunks ahead of the arithmetic (the barriers
+    // stop the scheduler from hoisting every load to the top, which would
+    // need more registers than a 1024-thread block has)
+#pragma unroll
+    for (int k = 0; k < D; ++k) load_chunk(k);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      if (k > 0 && k + D - 1 < VPT) load_chunk(k + D - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      arrive(k);
+      rank_sum(k);
+      emit_residual(k);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -587,8 +641,22 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   const double inv = 1.0 / sqrt(tot / (double)d + (double)a.eps);
 
   // ---- normalize, scale by gamma, store bf16 / FP4 / FP8
+  if constexpr (!ALL_AT_ONCE) {
+    fresh_offsets();
+    // keep h as floats: otherwise each (double)h of the sum of squares is
+    // reused here, and a wide row's doubles need twice the registers
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(h[k][e]));
+    load_gamma(0);
+  }
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
+    if constexpr (!ALL_AT_ONCE) {  // gamma one chunk ahead
+      if (k + 1 < VPT) load_gamma(k + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     float y[8];
     const float gg[8] = {g[k][0].x, g[k][0].y, g[k][0].z, g[k][0].w,
                          g[k][1].x, g[k][1].y, g[k][1].z, g[k][1].w};

@@ -132,6 +132,34 @@ def test_fp8_shapes(n, t, d):
     assert assert_fp8_close(got["fp8"], ref["fp8"]) <= 1e-4 * ref["fp8"].size
 
 
+# Rows wider than 16,384 elements: the kernel runs them as a pipeline of
+# chunks with loads one or two chunks ahead; ragged widths leave idle lanes in
+# the last chunk. (n, t, d, layout, outputs)
+WIDE = [(8, 3, 32768, 0, dict()), (8, 2, 32768, LL, dict(fp4=True)),
+        (8, 2, 65536, SENT, dict(fp8=2.0)), (3, 5, 40976, LL, dict(out=False, fp8=0.5)),
+        (8, 4, 24592, SENT, dict(fp4=True)), (5, 2, 65520, 0, dict(fp4=True))]
+
+
+@pytest.mark.parametrize("n,t,d,layout,kw", WIDE)
+def test_wide_rows(n, t, d, layout, kw):
+    ci = si.make_call(n, t, d, seed=90 + n, outlier_frac=0.3)
+    ref = orc().fused(ci.partials, ci.residual, ci.gamma, ci.eps, out=kw.get("out", True),
+                      fp4=kw.get("fp4", False), fp8_inv_scale=kw.get("fp8"))
+    info = arf.arfuse_query_launch(n, t, d)
+    note("wide n=%d t=%d d=%d layout=%d vpt=%d block=%d %s" % (n, t, d, layout, info.vpt,
+                                                              info.block, kw))
+    st = new_status()
+    got = run(ci, layout=layout, flag=ci.ll_base + 3, status=st, max_polls=1, **kw)
+    assert read_status(st) == (0, 0)
+    assert_residual_exact(got["residual_out"], ref["residual_out"])
+    if got["out"] is not None:
+        assert_y_close(got["out"], ref["y32"], ref["out"])
+    if got["codes"] is not None:
+        assert_fp4_close(got["codes"], got["scales"], ref["codes"], ref["scales"])
+    if got["fp8"] is not None:
+        assert_fp8_close(got["fp8"], ref["fp8"])
+
+
 # ------------------------------------------------------------ sentinel layout
 
 def test_sentinel_complete_data_matches_plain():
