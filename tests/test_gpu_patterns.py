@@ -239,6 +239,50 @@ def test_sentinel_allreduce_only_with_reset(t):
     assert_residual_exact(host_u16(ro), ref["residual_out"])
 
 
+@pytest.mark.parametrize("layout", [SENT, LL])
+def test_late_arrival_is_waited_for(layout):
+    """A producer on a second stream spins for about a millisecond, then copies
+    the partials into the slots, while the fused call, already running on the
+    current stream, re-reads them: it must see the data arrive (status clean)
+    and produce the oracle's result on it. The LL slots start as words with
+    the previous flag and a different payload, the sentinel slots as the
+    pattern."""
+    n, t, d = 4, 8, 4096
+    ci = si.make_call(n, t, d, seed=95)
+    flag = ci.ll_base + 7
+    if layout == LL:
+        data = [dev_u8(si.ll_pack(p, flag)) for p in ci.partials]
+        slots = [dev_u8(si.ll_pack(np.zeros_like(p), flag - 1)) for p in ci.partials]
+    else:
+        data = [dev_u16(p) for p in ci.partials]
+        slots = [torch.full((t, d), -1, dtype=torch.int16, device=DEV) for _ in range(n)]
+    res = dev_u16(ci.residual)
+    g = dev_f32(ci.gamma)
+    o = torch.empty((t, d), dtype=torch.bfloat16, device=DEV)
+    ro = torch.empty_like(o)
+    st = new_status()
+    producer = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    note("late arrival layout %d" % layout)
+    with torch.cuda.stream(producer):
+        torch.cuda._sleep(2_000_000)
+        for i in range(n):
+            arf.arfuse_stream_copy(slots[i], data[i])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    arf.arfuse_rmsnorm_ex(slots, res, g, float(ci.eps), o, ro, t=t, d=d, layout=layout,
+                          ll_flag=flag, max_polls=100_000, status=st)
+    e1.record()
+    torch.cuda.synchronize()
+    waited_ms = e0.elapsed_time(e1)
+    note("late arrival: the call took %.3f ms" % waited_ms)
+    assert waited_ms > 0.1, "the call did not wait: the test did not exercise the re-reads"
+    assert read_status(st) == (0, 0)
+    ref = orc().allreduce_rmsnorm(ci.partials, ci.residual, ci.gamma, ci.eps)
+    assert_residual_exact(host_u16(ro), ref["residual_out"])
+    assert_y_close(host_u16(o), ref["y32"], ref["out"])
+
+
 def test_sentinel_triple_buffered_chain_in_graph():
     n, t, d, k = 4, 8, 4096, 12
     ci = si.make_call(n, t, d, seed=82)
