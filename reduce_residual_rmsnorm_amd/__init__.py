@@ -116,6 +116,47 @@ def _addr(x) -> int:
     return int(x.data_ptr())
 
 
+def _buf(x, nbytes: int, name: str) -> int:
+    """Device address of a buffer argument. A tensor must live on a GPU, be
+    contiguous and hold at least `nbytes` bytes (any dtype: bf16 data may come
+    as a bfloat16, int16 or uint8 view); an int is taken as a raw device
+    address; None is NULL. Checked here because the C ABI receives bare
+    pointers: a host tensor's address would make the kernel fault."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if not x.is_cuda:
+        raise ValueError("%s must be a GPU tensor (got device %s)" % (name, x.device))
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    have = x.numel() * x.element_size()
+    if have < nbytes:
+        raise ValueError("%s holds %d bytes; the call needs %d" % (name, have, nbytes))
+    return int(x.data_ptr())
+
+
+def _call_buffers(partials, residual, gamma, out, residual_out, fp4_out, fp4_scales, t, d,
+                  layout=ARFUSE_LAYOUT_PLAIN, fp8_out=None, status=None, reset=None):
+    """Checked addresses of every buffer of a fused call (see _buf)."""
+    plane = t * d * 2
+    pbytes = 2 * plane if layout == ARFUSE_LAYOUT_LL else plane
+    arr = (ctypes.c_void_p * len(partials))(
+        *[_buf(p, pbytes, "partials[%d]" % i) for i, p in enumerate(partials)])
+    return dict(
+        arr=arr,
+        residual=_buf(residual, plane, "residual"),
+        gamma=_buf(gamma, 4 * d if t else 0, "gamma"),
+        out=_buf(out, plane, "out"),
+        residual_out=_buf(residual_out, plane, "residual_out"),
+        fp4_out=_buf(fp4_out, t * d // 2, "fp4_out"),
+        fp4_scales=_buf(fp4_scales, t * d // 16, "fp4_scales"),
+        fp8_out=_buf(fp8_out, t * d, "fp8_out"),
+        status=_buf(status, 16, "status"),
+        reset=None if reset is None else [_buf(r, plane, "reset[%d]" % i)
+                                          for i, r in enumerate(reset)])
+
+
 def _stream(stream) -> int:
     if stream is None:
         import torch
@@ -160,9 +201,9 @@ def arfuse_rmsnorm(partials: Sequence, residual, gamma, eps: float, out, residua
     """Fused call on plain bf16 partials; see arfuse_rmsnorm in include/arfuse.h.
     Tensors (or int device addresses with explicit t, d) are passed through."""
     t, d = _td(residual, t, d)
-    arr = (ctypes.c_void_p * len(partials))(*[_addr(p) for p in partials])
-    rc = lib.arfuse_rmsnorm(arr, len(partials), _addr(residual), _addr(gamma), float(eps),
-                            _addr(out), _addr(residual_out), _addr(fp4_out), _addr(fp4_scales),
+    b = _call_buffers(partials, residual, gamma, out, residual_out, fp4_out, fp4_scales, t, d)
+    rc = lib.arfuse_rmsnorm(b["arr"], len(partials), b["residual"], b["gamma"], float(eps),
+                            b["out"], b["residual_out"], b["fp4_out"], b["fp4_scales"],
                             t, d, _stream(stream))
     _check(rc, "arfuse_rmsnorm")
 
@@ -176,12 +217,13 @@ def arfuse_rmsnorm_ex(partials: Sequence, residual, gamma, eps: float, out, resi
     residual and gamma may be None (the no-residual and all-reduce-only
     patterns); then pass t and d explicitly."""
     t, d = _td(residual, t, d)
-    arr = (ctypes.c_void_p * len(partials))(*[_addr(p) for p in partials])
-    o = _opts(layout, ll_flag, max_polls, status, block_threads, vpt, sentinel, reset, fp8_out,
-              fp8_inv_scale)
-    rc = lib.arfuse_rmsnorm_ex(arr, len(partials), _addr(residual), _addr(gamma), float(eps),
-                               _addr(out), _addr(residual_out), _addr(fp4_out),
-                               _addr(fp4_scales), t, d, _stream(stream), ctypes.byref(o))
+    b = _call_buffers(partials, residual, gamma, out, residual_out, fp4_out, fp4_scales, t, d,
+                      layout=layout, fp8_out=fp8_out, status=status, reset=reset)
+    o = _opts(layout, ll_flag, max_polls, b["status"], block_threads, vpt, sentinel, b["reset"],
+              b["fp8_out"], fp8_inv_scale)
+    rc = lib.arfuse_rmsnorm_ex(b["arr"], len(partials), b["residual"], b["gamma"], float(eps),
+                               b["out"], b["residual_out"], b["fp4_out"], b["fp4_scales"],
+                               t, d, _stream(stream), ctypes.byref(o))
     _check(rc, "arfuse_rmsnorm_ex")
 
 
@@ -189,8 +231,9 @@ def arfuse_quantize_fp4(y, codes, scales, stream=None, t=None, d=None) -> None:
     """FP4 epilogue alone on fp32 y [t][d]; see include/arfuse.h."""
     if t is None or d is None:
         t, d = y.shape
-    rc = lib.arfuse_quantize_fp4(_addr(y), int(t), int(d), _addr(codes), _addr(scales),
-                                 _stream(stream))
+    t, d = int(t), int(d)
+    rc = lib.arfuse_quantize_fp4(_buf(y, 4 * t * d, "y"), t, d, _buf(codes, t * d // 2, "codes"),
+                                 _buf(scales, t * d // 16, "scales"), _stream(stream))
     _check(rc, "arfuse_quantize_fp4")
 
 
@@ -215,19 +258,23 @@ def arfuse_launch_floor(n_partials: int, t: int, d: int, epilogue: int = ARFUSE_
 def arfuse_stream_copy(dst, src, nbytes: Optional[int] = None, stream=None) -> None:
     if nbytes is None:
         nbytes = src.numel() * src.element_size()
-    rc = lib.arfuse_stream_copy(_addr(dst), _addr(src), int(nbytes), _stream(stream))
+    nbytes = int(nbytes)
+    rc = lib.arfuse_stream_copy(_buf(dst, nbytes, "dst"), _buf(src, nbytes, "src"), nbytes,
+                                _stream(stream))
     _check(rc, "arfuse_stream_copy")
 
 
 def arfuse_round_bf16(x, out, stream=None) -> None:
     """Test entry: the kernel's fp32 -> bf16 rounding of x into out."""
-    rc = lib.arfuse_round_bf16(_addr(x), int(x.numel()), _addr(out), _stream(stream))
+    n = int(x.numel())
+    rc = lib.arfuse_round_bf16(_buf(x, 4 * n, "x"), n, _buf(out, 2 * n, "out"), _stream(stream))
     _check(rc, "arfuse_round_bf16")
 
 
 def arfuse_round_fp8(x, out, stream=None) -> None:
     """Test entry: the kernel's FP8 conversion (inv_scale 1) of x into out."""
-    rc = lib.arfuse_round_fp8(_addr(x), int(x.numel()), _addr(out), _stream(stream))
+    n = int(x.numel())
+    rc = lib.arfuse_round_fp8(_buf(x, 4 * n, "x"), n, _buf(out, n, "out"), _stream(stream))
     _check(rc, "arfuse_round_fp8")
 
 

@@ -239,3 +239,42 @@ def test_single_hip_runtime_in_process():
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
                        check=True)
     assert r.stdout.strip() == "1", r.stdout + r.stderr
+
+
+def test_binding_rejects_host_small_and_strided_tensors():
+    """The binding checks tensors before the C call: a host tensor's address
+    would make the kernel fault, a short or strided one would be read past its
+    end or in the wrong order. (Raw int addresses are passed through.)"""
+    import torch
+    t, d = 2, 64
+    cpu = torch.zeros(t, d, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        arf.arfuse_rmsnorm([cpu], cpu, torch.ones(d), 1e-5, cpu, cpu)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        arf.arfuse_stream_copy(torch.zeros(16, dtype=torch.uint8), torch.zeros(16, dtype=torch.uint8))
+
+    class FakeCuda:
+        """A stand-in for a GPU tensor (no GPU here): shape facts only."""
+        def __init__(self, nbytes, contiguous=True):
+            self.is_cuda, self._n, self._c, self.device = True, nbytes, contiguous, "cuda:0"
+            self.shape = (t, d)
+        def is_contiguous(self):
+            return self._c
+        def numel(self):
+            return self._n
+        def element_size(self):
+            return 1
+        def data_ptr(self):
+            return spaced(50)
+
+    plane = t * d * 2
+    ok = FakeCuda(plane)
+    with pytest.raises(ValueError, match="holds 255 bytes"):
+        arf.arfuse_rmsnorm([FakeCuda(plane - 1)], ok, FakeCuda(4 * d), 1e-5, ok, FakeCuda(plane))
+    with pytest.raises(ValueError, match="contiguous"):
+        arf.arfuse_rmsnorm([ok], ok, FakeCuda(4 * d), 1e-5, FakeCuda(plane, contiguous=False), ok)
+    with pytest.raises(ValueError, match="partials\\[0\\] holds"):   # LL words are twice the bytes
+        arf.arfuse_rmsnorm_ex([FakeCuda(plane)], ok, FakeCuda(4 * d), 1e-5, ok, ok,
+                              layout=arf.ARFUSE_LAYOUT_LL)
+    with pytest.raises(ValueError, match="status"):
+        arf.arfuse_rmsnorm_ex([ok], ok, FakeCuda(4 * d), 1e-5, ok, ok, status=FakeCuda(8))
