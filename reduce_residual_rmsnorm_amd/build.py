@@ -43,20 +43,10 @@ FLAGS = [
     "-Wno-unused-function",
 ]
 
-# Kernel-argument preloading: the dispatch loads the row kernel's leading
-# scalar arguments (row width, flags, residual, then partials) into scalar
-# registers, up to 14 of them. That covers every partial pointer up to N = 5,
-# and there the rows start loading without an argument fetch (measured
-# 0.06-0.13 us less per decode call); from N = 6 the remaining pointers still
-# need one, and preloading measured no better.
-PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=9"]
-PRELOAD_MAX_N = 5  # kLeadMaxN in arfuse_device.hpp
-
 
 def _jobs():
     units = [(SRC, [], "arfuse")]
-    units += [(ROWS, ["-DARFUSE_N=%d" % n] + (PRELOAD if n <= PRELOAD_MAX_N else []), "rows_n%d" % n)
-              for n in range(1, 9)]
+    units += [(ROWS, ["-DARFUSE_N=%d" % n], "rows_n%d" % n) for n in range(1, 9)]
     return units
 
 

@@ -1,4 +1,4 @@
-// arfuse — fused all-reduce epilogue + residual add + RMSNorm (+ FP4/FP8) for
+// arfuse — fused all-reduce epilogue + residual add + RMSNorm (+ FP4) for
 // gfx950 (MI355X). The C ABI declared in include/arfuse.h and its auxiliary
 // kernels; the device helpers and the row kernel are in arfuse_device.hpp.
 //
@@ -9,14 +9,13 @@
 //    elements per vector; consecutive lanes touch consecutive 16 bytes, so
 //    every wave load is one fully coalesced 1 KiB transaction per partial.
 //  * Every load of the row (N partials, residual, gamma) is issued before any
-//    arithmetic while the row fits the registers at once; wider rows run as a
-//    pipeline of chunks with loads one or two chunks ahead.
+//    arithmetic, so a thread keeps N+2 independent 16-byte loads in flight.
 //  * h stays in VGPRs between the sum and the normalize: no intermediate HBM
 //    round trip (Deep Dive: AllReduce and AllReduce Fusion in TensorRT-LLM,
 //    §6.1 and §6.4).
-//  * The row's sum of squares is reduced across the wave with DPP moves, then
-//    across waves through one LDS slot per wave, summed in wave order by every
-//    thread (a fixed tree: deterministic, no atomics).
+//  * The row's sum of squares is reduced across the wave with XOR shuffles,
+//    then across waves through one LDS slot per wave, summed in wave order by
+//    every thread (a fixed tree: deterministic, no atomics).
 //  * Ragged rows (d/8 not a multiple of the block) clamp the vector index of
 //    idle lanes to the last vector, so all loads stay unconditional and in
 //    bounds; clamped lanes store nothing and add nothing.
@@ -40,7 +39,7 @@ namespace arfuse_detail {
 namespace {
 
 // Same argument block and launch shape as row_kernel, no work: the floor.
-__global__ __launch_bounds__(kMaxBlock) void floor_kernel(ARFUSE_ROW_PARAMS) {}
+__global__ __launch_bounds__(kMaxBlock) void floor_kernel(RowArgs) {}
 
 // FP4 of fp32 y [t][d]: thread i owns global 16-byte-bf16-vector index i
 // (8 fp32 values); rows hold an even number of such vectors, so the pair
@@ -117,22 +116,6 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 Range range_of(const void* p, int64_t bytes) {
   return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes};
-}
-
-// Launch of a row kernel (or the empty floor kernel with the same
-// parameters): the leading scalar arguments repeat the argument block's row
-// width, flags, residual and first six partials (see ARFUSE_ROW_PARAMS).
-int launch_row(const void* fn, const RowArgs& a, int64_t grid, int block, void* stream) {
-  uint32_t d8 = (uint32_t)a.d8;
-  uint32_t flags = a.flags;
-  const char* res = (const char*)a.residual;
-  const char* p[6];
-  for (int i = 0; i < 6; ++i) p[i] = (const char*)a.part[i];
-  RowArgs blk = a;
-  void* args[] = {&d8, &flags, &res, &p[0], &p[1], &p[2], &p[3], &p[4], &p[5], &blk};
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)block), args, 0,
-                                 (hipStream_t)stream);
-  return launch_status(e);
 }
 
 // Launch shape: the smallest VPT in {1, 2, 4, 8} whose 1024-thread block
@@ -290,7 +273,10 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
 
   const void* fn = (const void*)select_row_kernel(n, vpt, layout, epi);
   if (!fn) return ARFUSE_ERR_UNSUPPORTED;
-  return launch_row(fn, a, t + extra, block, stream);
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(t + extra)), dim3((unsigned)block), args, 0,
+                                 (hipStream_t)stream);
+  return launch_status(e);
 }
 
 }  // namespace
@@ -365,7 +351,10 @@ int arfuse_launch_floor(int n_partials, int64_t t, int64_t d, int epilogue,
   const bool reset = opts && opts->layout == ARFUSE_LAYOUT_SENTINEL && opts->reset;
   const int64_t grid = t + reset_blocks(n_partials, t, d, block, reset);
   RowArgs a = {};
-  return launch_row((const void*)floor_kernel, a, grid, block, stream);
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel((const void*)floor_kernel, dim3((unsigned)grid), dim3((unsigned)block),
+                                 args, 0, (hipStream_t)stream);
+  return launch_status(e);
 }
 
 int arfuse_stream_copy(void* dst, const void* src, int64_t bytes, void* stream) {

@@ -371,22 +371,8 @@ constexpr int pipeline_depth() {
   return 1;
 }
 
-// The row kernel's leading arguments are the fields every row needs first:
-// the row width (16-byte vectors), the flags, the residual and the first six
-// partials. As plain scalar arguments ahead of the argument block, gfx950 can
-// preload them into scalar registers at dispatch (the instances up to
-// kLeadMaxN partials are built with -amdgpu-kernarg-preload-count; 14
-// registers cover the residual and five partials), so a row's first loads wait
-// for no argument fetch. The argument block repeats them and holds the rest;
-// instances with more partials read everything from it, in one scalar load of
-// the eight partial pointers.
-constexpr int kLeadMaxN = 5;
-#define ARFUSE_ROW_PARAMS                                                                      \
-  uint32_t d8, uint32_t flags, const char* res, const char* p0, const char* p1, const char* p2, \
-      const char* p3, const char* p4, const char* p5, RowArgs a
-
 template <int N, int VPT, bool LL, bool SENT, int EPI>
-__global__ __launch_bounds__(kMaxBlock) void row_kernel(ARFUSE_ROW_PARAMS) {
+__global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   constexpr bool NORM = EPI != 0;
   constexpr bool OUT = (EPI & ARFUSE_EPI_BF16) != 0;
   constexpr bool FP4 = (EPI & ARFUSE_EPI_FP4) != 0;
@@ -413,27 +399,17 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(ARFUSE_ROW_PARAMS) {
       return;
     }
   }
-  constexpr bool LEAD = N <= kLeadMaxN;
-  if constexpr (!LEAD) {
-    d8 = (uint32_t)a.d8;
-    flags = a.flags;
-    res = (const char*)a.residual;
-  }
-  const uint32_t d = d8 * 8;
+  const uint32_t d = (uint32_t)(a.d8 * 8);
   const int64_t rb = (int64_t)blockIdx.x * d;  // first element of the row
-  const bool has_res = (flags & kHasResidual) != 0;
-  const bool has_rout = (flags & kHasResidualOut) != 0;
+  const bool has_res = (a.flags & kHasResidual) != 0;
+  const bool has_rout = (a.flags & kHasResidualOut) != 0;
 
   // row bases: partials (bf16, or LL words of 4 bytes per element), residual,
   // outputs (bf16), FP4 codes (half a byte per element), scales (1/16), FP8
   const char* prow[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const char* base = !LEAD ? (const char*)a.part[i]
-                     : i == 0 ? p0 : i == 1 ? p1 : i == 2 ? p2 : i == 3 ? p3 : i == 4 ? p4 : p5;
-    prow[i] = base + rb * (LL ? 4 : 2);
-  }
-  const char* rrow = res + rb * 2;
+  for (int i = 0; i < N; ++i) prow[i] = (const char*)a.part[i] + rb * (LL ? 4 : 2);
+  const char* rrow = (const char*)a.residual + rb * 2;
   const char* grow = (const char*)a.gamma;
   char* orow = (char*)a.residual_out + rb * 2;
   char* yrow = (char*)a.out + rb * 2;
@@ -596,7 +572,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(ARFUSE_ROW_PARAMS) {
   // row's data no longer occupy registers
   auto reset_row = [&]() {
     if constexpr (SENT) {
-      if (flags & kReset) {
+      if (a.flags & kReset) {
         if constexpr (!ALL_AT_ONCE) fresh_offsets();
         const u32x4 sv = {a.sentinel2, a.sentinel2, a.sentinel2, a.sentinel2};
 #pragma unroll
@@ -728,7 +704,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(ARFUSE_ROW_PARAMS) {
   reset_row();
 }
 
-typedef void (*RowFn)(ARFUSE_ROW_PARAMS);
+typedef void (*RowFn)(RowArgs);
 
 // Instances for one rank count: returns the kernel for (VPT, layout, EPI);
 // layout is ARFUSE_LAYOUT_PLAIN, _LL or _SENTINEL.
