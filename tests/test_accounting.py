@@ -58,6 +58,34 @@ def test_algorithmic_bytes_add_the_slot_reads():
     assert rd == 8 * 2 * 131072 + 131072 + 4 * 8192
 
 
+def test_algorithmic_bytes_of_the_patterns():
+    """Each fusion pattern moves what it reads and writes: no residual read
+    without a residual; without gamma neither gamma nor any norm output; FP8
+    one byte per element; a sentinel reset writes the N slot planes again."""
+    n, t, d = 8, 4096, 8192
+    P = bench.plane_bytes(t, d)
+    base_rd, base_wr = bench.algorithmic_bytes(n, t, d)
+    assert bench.algorithmic_bytes(n, t, d, residual=False) == (base_rd - P, base_wr)
+    assert bench.algorithmic_bytes(n, t, d, norm=False) == (n * P + P, P)
+    assert bench.algorithmic_bytes(n, t, d, norm=False, fp4=True, fp8=True) == (n * P + P, P)
+    assert bench.algorithmic_bytes(n, t, d, out=False, fp8=True) == (base_rd, P + t * d)
+    assert bench.algorithmic_bytes(n, t, d, rout=False) == (base_rd, base_wr - P)
+    assert bench.algorithmic_bytes(n, t, d, reset=True) == (base_rd, base_wr + n * P)
+    # the per-call figures quoted for these patterns at this shape
+    assert sum(bench.algorithmic_bytes(n, t, d, norm=False)) == 671088640
+    assert sum(bench.algorithmic_bytes(n, t, d, out=False, fp8=True)) == 704675840
+    assert sum(bench.algorithmic_bytes(n, t, d, reset=True)) == 1275101184
+
+
+def test_extras_table_labels_and_modes():
+    """The secondary measurements are named by their shapes and modes."""
+    t = bench.extra_table()
+    assert "decode_n8_t8_d8192_chain160_sentinel_fresh" in t
+    assert "prefill_n8_t512_d65536" in t
+    assert all(callable(f) for f in t.values())
+    assert set(bench.DECODE_PROFILED) <= set(t)
+
+
 @pytest.mark.parametrize("call_bytes,sets", [(738230272, 2), (92307456, 7), (1, 2 * 256 * 2 ** 20 + 1)])
 def test_rotation_defeats_infinity_cache(call_bytes, sets):
     n = bench.n_sets_for(call_bytes)
