@@ -379,16 +379,16 @@ DECODE_PROFILED = ("decode_n8_t8_d8192_chain160", "decode_n8_t8_d8192_chain160_l
 
 PROFILE_COMMANDS = {
     "trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
-             "-d $REPO/gpurun_out/prof_trace -o prefill -- python3 $REPO/bench.py --steps 50 "
+             "-d $OUT/prof_trace -o prefill -- python3 $REPO/bench.py --steps 50 "
              "--warmup 5 --no-extras --no-cpu-baseline",
     "pmc_prefill": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {C} --kernel-include-regex "
-                   "row_kernel -f csv -d $REPO/gpurun_out/pmc_prefill_{C} -o pmc -- python3 "
+                   "row_kernel -f csv -d $OUT/pmc_prefill_{C} -o pmc -- python3 "
                    "$REPO/bench.py --steps 5 --warmup 1 --no-extras --no-cpu-baseline",
     "pmc_copy": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {C} --kernel-include-regex "
-                "copy_kernel -f csv -d $REPO/gpurun_out/pmc_copy_{C} -o pmc -- python3 "
+                "copy_kernel -f csv -d $OUT/pmc_copy_{C} -o pmc -- python3 "
                 "$REPO/bench.py --copy-only",
     "trace_decode": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
-                    "-d $REPO/gpurun_out/prof_decode -o decode -- python3 $REPO/bench.py "
+                    "-d $OUT/prof_decode -o decode -- python3 $REPO/bench.py "
                     + " ".join("--only-extra " + x for x in DECODE_PROFILED),
 }
 
@@ -409,14 +409,15 @@ def _counter(path, kname):
 
 def summarize_profiles(outdir: str) -> None:
     """Write profiles/row_kernel_<workload>_{stats.md,traffic.json} from the
-    rocprofv3 outputs of PROFILE_COMMANDS under `outdir` (gpurun_out/)."""
+    rocprofv3 outputs of PROFILE_COMMANDS under `outdir` (their $OUT)."""
     import csv
     name = "prefill_n8_t4096_d8192"
     os.makedirs(PROFILES, exist_ok=True)
     line = _bench_line(os.path.join(outdir, "prof_trace.log"))
     rows = list(csv.DictReader(open(os.path.join(outdir, "prof_trace", "prefill_kernel_stats.csv"))))
     md = ["# row_kernel, %s: rocprofv3 kernel statistics" % name, "",
-          "Command (`$REPO` is the repository root):", "", "    " + PROFILE_COMMANDS["trace"], "",
+          "Command (`$REPO` is the repository root, `$OUT` the output directory):", "",
+          "    " + PROFILE_COMMANDS["trace"], "",
           "Kernel source sha256[:16]: `%s`" % (line or {}).get("kernel_source", "?"), "",
           "| kernel | calls | average µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
     for r in rows:
@@ -469,7 +470,8 @@ def summarize_decode_profile(outdir: str) -> None:
     line = _bench_line(os.path.join(outdir, "prof_decode.log")) or {}
     rows = list(csv.DictReader(open(os.path.join(outdir, "prof_decode", "decode_kernel_stats.csv"))))
     md = ["# row_kernel, decode chains: rocprofv3 kernel statistics", "",
-          "Command (`$REPO` is the repository root):", "", "    " + PROFILE_COMMANDS["trace_decode"], "",
+          "Command (`$REPO` is the repository root, `$OUT` the output directory):", "",
+          "    " + PROFILE_COMMANDS["trace_decode"], "",
           "Kernel source sha256[:16]: `%s`" % line.get("kernel_source", "?"), "",
           "Each chain is captured once in a graph and replayed (5 warm-up + 200 timed "
           "replays), then the same-length graph of the empty kernel is replayed. Every "
@@ -570,7 +572,7 @@ def main(argv=None):
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
         return 2
 
