@@ -207,14 +207,16 @@ def time_graph(g, reps: int):
 
 def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = False,
                  out: bool = True, reps: int = 200, seed: int = 0, fp8: bool = False,
-                 sentinel: bool = False, fresh=None):
+                 sentinel: bool = False, fresh=None, split: int = 0):
     """µs per call of a k-call chain captured in one graph (call c reads call
     c-1's residual_out), and of the same-length graph of the empty kernel
     with the same launch (the per-node floor). `sentinel` reads the slots in
     the sentinel layout and refills a second slot set on every call (the
     triple-buffer reset), `fp8` adds the FP8 output. `fresh` (default: LL
     only) gives every call its own partial buffers, as a peer's push would,
-    instead of re-reading one set that stays in the caches."""
+    instead of re-reading one set that stays in the caches. `split` > 1
+    divides every row among that many workgroups (sums of squares exchanged
+    through a zeroed workspace)."""
     import numpy as np
     import torch
 
@@ -241,6 +243,8 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
     status = torch.zeros(4, dtype=torch.int32, device=_dev())
     f8 = torch.empty((t, d), dtype=torch.uint8, device=_dev()) if fp8 else None
     slots = [torch.empty_like(res0) for _ in range(n)] if sentinel else None
+    ws = torch.zeros(16 * t * split, dtype=torch.uint8, device=_dev()) if split > 1 else None
+    sx = dict(split=split, workspace=ws)
     epi = ((arf.ARFUSE_EPI_BF16 if out else 0) | (arf.ARFUSE_EPI_FP4 if fp4 else 0)
            | (arf.ARFUSE_EPI_FP8 if fp8 else 0))
 
@@ -251,12 +255,12 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
             if ll:
                 arf.arfuse_rmsnorm_ex(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales,
                                       layout=arf.ARFUSE_LAYOUT_LL, ll_flag=flags[c], max_polls=4,
-                                      status=status)
-            elif sentinel or fp8:
+                                      status=status, **sx)
+            elif sentinel or fp8 or split > 1:
                 arf.arfuse_rmsnorm_ex(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales,
                                       layout=arf.ARFUSE_LAYOUT_SENTINEL if sentinel else 0,
                                       max_polls=4, status=status, reset=slots, fp8_out=f8,
-                                      fp8_inv_scale=4.0)
+                                      fp8_inv_scale=4.0, **sx)
             else:
                 arf.arfuse_rmsnorm(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales)
 
@@ -264,7 +268,7 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
         lay = (arf.ARFUSE_LAYOUT_LL if ll else
                arf.ARFUSE_LAYOUT_SENTINEL if sentinel else arf.ARFUSE_LAYOUT_PLAIN)
         for _ in range(k):
-            arf.arfuse_launch_floor(n, t, d, epi, layout=lay)
+            arf.arfuse_launch_floor(n, t, d, epi, layout=lay, split=split)
 
     enqueue()
     torch.cuda.synchronize()
@@ -279,8 +283,9 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
     st = status.cpu().numpy().view(np.uint32)
     if st[0] != 0:
         raise RuntimeError("arrival reported bad during the benchmark: %s" % st)
-    info = arf.arfuse_query_launch(n, t, d, epi)
+    info = arf.arfuse_query_launch(n, t, d, epi, split=split)
     r = dict(n=n, t=t, d=d, calls=k, layout="ll" if ll else "sentinel" if sentinel else "plain",
+             split=max(1, split),
              fp4=fp4, fp8=fp8, reset=sentinel, fresh_partials=bool(fresh),
              grid=int(info.grid), block=int(info.block),
              us_per_call_p50=chain["p50"] / k, chain_us_p50=chain["p50"],
@@ -528,12 +533,22 @@ def extra_table():
             (8, 8, 8192, 160, "fp8", False, "decode_n8_t8_d8192_chain160_fp8"),
             (4, 1, 8192, 100, "", True, "fp4_n4_t1_d8192_x100"),
             (4, 8, 8192, 100, "", True, "fp4_n4_t8_d8192_x100"),
-            (4, 64, 8192, 100, "", True, "fp4_n4_t64_d8192_x100")]:
-        t[label] = (lambda nn=nn, tt=tt, dd=dd, kk=kk, mode=mode, fp4=fp4:
+            (4, 64, 8192, 100, "", True, "fp4_n4_t64_d8192_x100"),
+            # split rows: 2, 4 or 8 workgroups per row
+            (4, 8, 8192, 160, "split4", False, "decode_n4_t8_d8192_chain160_split4"),
+            (8, 8, 8192, 160, "split2", False, "decode_n8_t8_d8192_chain160_split2"),
+            (8, 8, 8192, 160, "split4", False, "decode_n8_t8_d8192_chain160_split4"),
+            (8, 8, 8192, 160, "split8", False, "decode_n8_t8_d8192_chain160_split8"),
+            (8, 8, 8192, 160, "ll_split4", False, "decode_n8_t8_d8192_chain160_ll_split4"),
+            (8, 8, 8192, 160, "sentinel_split4", False, "decode_n8_t8_d8192_chain160_sentinel_split4"),
+            (4, 1, 8192, 100, "split8", True, "fp4_n4_t1_d8192_x100_split8"),
+            (4, 8, 8192, 100, "split4", True, "fp4_n4_t8_d8192_x100_split4")]:
+        sp = int(mode.split("split")[1]) if "split" in mode else 0
+        t[label] = (lambda nn=nn, tt=tt, dd=dd, kk=kk, mode=mode, fp4=fp4, sp=sp:
                     decode_chain(nn, tt, dd, kk, ll=mode.startswith("ll"), fp4=fp4, out=not fp4,
                                  sentinel=mode.startswith("sentinel"), fp8=mode == "fp8",
                                  fresh=(True if "fresh" in mode else False if "reused" in mode
-                                        else None)))
+                                        else None), split=sp))
     return t
 
 

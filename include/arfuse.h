@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define ARFUSE_VERSION 1
+#define ARFUSE_VERSION 2
 
 /* Largest supported rank count and row width. */
 #define ARFUSE_MAX_PARTIALS 8
@@ -113,16 +113,27 @@ typedef enum {
 #define ARFUSE_EPI_FP8 4  /* opts->fp8_out (not together with FP4) */
 /* A mask of 0 is the all-reduce alone (no gamma): only residual_out. */
 
-/* Device-side status of an LL call. The caller zeroes it before the call
- * (the library only ever ORs into code and adds to bad_words, so one word
- * can collect several calls, e.g. a captured chain). */
+/* Device-side status of a call (LL or sentinel layout, split rows). The
+ * caller zeroes it before the call (the library only ever ORs into code and
+ * adds to the counters, so one word can collect several calls, e.g. a
+ * captured chain). */
 typedef struct {
-  uint32_t code;      /* 0, or ARFUSE_ERR_FLAG_TIMEOUT */
-  uint32_t reserved;
+  uint32_t code;      /* 0, or ARFUSE_ERR_FLAG_TIMEOUT: something a row waits
+                         for did not arrive within its bounded wait */
+  uint32_t exchange_timeouts; /* split rows: partner slots that did not
+                         carry this call's sequence within the bounded wait,
+                         or carried a later one (the workspace is out of step
+                         with the calls); that row's outputs are unspecified */
   uint64_t bad_words; /* LL words whose flag never matched, or, in the
                          sentinel layout, 16-byte vectors that still held the
                          sentinel after the last re-read */
 } arfuse_ll_status;
+
+/* Split rows: largest number of workgroups per row, and the largest
+ * t * split a call may launch (every workgroup of a row must be resident at
+ * once for the exchange). */
+#define ARFUSE_MAX_SPLIT 8
+#define ARFUSE_MAX_SPLIT_BLOCKS 256
 
 /* Options of arfuse_rmsnorm_ex. Zero-initialise it for the defaults
  * (plain layout, library-chosen launch). */
@@ -140,7 +151,14 @@ typedef struct {
                                  per partial, 1, 2, 4 or 8; 0 = auto */
   uint32_t sentinel;          /* SENTINEL: 16-bit pattern of a not-yet-
                                  written element; 0 = ARFUSE_SENTINEL_DEFAULT */
-  uint32_t reserved;          /* must be 0 */
+  uint32_t split;             /* workgroups per row: 0 or 1 = one; 2, 4 or 8
+                                 divide each row's columns between that many
+                                 workgroups on different CUs, which exchange
+                                 the row's sum of squares through workspace
+                                 (decode shapes, where a row is bound by one
+                                 CU's issue rate). Needs workspace,
+                                 d % (16 * split) == 0 and
+                                 t * split <= ARFUSE_MAX_SPLIT_BLOCKS */
   void* const* reset;         /* SENTINEL: (host) array of n_partials (device)
                                  bf16 [t][d] buffers, 16-byte aligned, that this
                                  call fills with the sentinel (the slot set a
@@ -152,15 +170,27 @@ typedef struct {
                                  448), 16-byte aligned; or NULL */
   float fp8_inv_scale;        /* per-tensor reciprocal FP8 scale, finite */
   uint32_t reserved2;         /* must be 0 */
+  void* workspace;            /* split rows: (device) t * split 16-byte slots,
+                                 16-byte aligned, zeroed before the first call
+                                 (arfuse_query_launch gives the size). Each
+                                 slot carries a sequence that every call
+                                 advances, so the workspace stays valid across
+                                 calls and graph replays of the same t and
+                                 split; zero it again when either changes.
+                                 Calls sharing a workspace must not overlap.
+                                 NULL when split <= 1 */
 } arfuse_opts;
 
 /* The launch the library would use for a call. */
 typedef struct {
-  int64_t grid;         /* workgroups: one per token row, plus, in the
+  int64_t grid;         /* workgroups: split per token row, plus, in the
                            sentinel layout with a reset set and t <= 128,
                            the blocks that write the reset */
   int32_t block;        /* threads per workgroup */
   int32_t vpt;          /* 16-byte vectors per thread per partial */
+  int32_t split;        /* workgroups per row (1 unless opts->split > 1) */
+  int32_t reserved;
+  int64_t workspace_bytes; /* bytes of opts->workspace a split call needs */
 } arfuse_launch_info;
 
 /*
@@ -204,6 +234,16 @@ int arfuse_rmsnorm(const void* const* partials, int n_partials, const void* resi
  * that never arrive are counted into opts->status (if given); the rows
  * holding them get unspecified outputs. The kernel never waits without
  * bound. opts->fp8_out requests the FP8 output.
+ *
+ * opts->split > 1 divides every row's columns between that many workgroups
+ * (on different CUs). Each computes its columns' share of the sum of squares,
+ * writes it with the next sequence to its slot of opts->workspace and waits
+ * (bounded) for the row's other slots to carry the same sequence; the shares
+ * are added in slice order, so the result is deterministic (it may differ in
+ * the last bits from the unsplit call, whose sum runs in another order).
+ * residual_out, the FP4 and the FP8 outputs are produced per slice exactly as
+ * without the split. A share that does not arrive, or a slot already carrying
+ * a later sequence, is counted into opts->status (exchange_timeouts).
  */
 int arfuse_rmsnorm_ex(const void* const* partials, int n_partials, const void* residual,
                       const float* gamma, float eps, void* out, void* residual_out,

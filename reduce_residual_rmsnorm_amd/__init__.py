@@ -30,6 +30,8 @@ ARFUSE_EPI_FP4 = 2
 ARFUSE_MAX_PARTIALS = 8
 ARFUSE_MAX_D = 65536
 ARFUSE_MAX_POLLS = 1 << 20
+ARFUSE_MAX_SPLIT = 8
+ARFUSE_MAX_SPLIT_BLOCKS = 256
 
 # The exported functions, as declared in include/arfuse.h.
 EXPORTED = ("arfuse_rmsnorm", "arfuse_rmsnorm_ex", "arfuse_quantize_fp4", "arfuse_query_launch",
@@ -48,7 +50,7 @@ class ArfuseError(RuntimeError):
 
 
 class arfuse_ll_status(ctypes.Structure):
-    _fields_ = [("code", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+    _fields_ = [("code", ctypes.c_uint32), ("exchange_timeouts", ctypes.c_uint32),
                 ("bad_words", ctypes.c_uint64)]
 
 
@@ -56,13 +58,16 @@ class arfuse_opts(ctypes.Structure):
     _fields_ = [("layout", ctypes.c_int32), ("max_polls", ctypes.c_uint32),
                 ("ll_flag", ctypes.c_uint64), ("status", ctypes.c_void_p),
                 ("block_threads", ctypes.c_int32), ("vpt", ctypes.c_int32),
-                ("sentinel", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("sentinel", ctypes.c_uint32), ("split", ctypes.c_uint32),
                 ("reset", ctypes.c_void_p), ("fp8_out", ctypes.c_void_p),
-                ("fp8_inv_scale", ctypes.c_float), ("reserved2", ctypes.c_uint32)]
+                ("fp8_inv_scale", ctypes.c_float), ("reserved2", ctypes.c_uint32),
+                ("workspace", ctypes.c_void_p)]
 
 
 class arfuse_launch_info(ctypes.Structure):
-    _fields_ = [("grid", ctypes.c_int64), ("block", ctypes.c_int32), ("vpt", ctypes.c_int32)]
+    _fields_ = [("grid", ctypes.c_int64), ("block", ctypes.c_int32), ("vpt", ctypes.c_int32),
+                ("split", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64)]
 
 
 def _load(path: str = LIB_PATH):
@@ -137,7 +142,8 @@ def _buf(x, nbytes: int, name: str) -> int:
 
 
 def _call_buffers(partials, residual, gamma, out, residual_out, fp4_out, fp4_scales, t, d,
-                  layout=ARFUSE_LAYOUT_PLAIN, fp8_out=None, status=None, reset=None):
+                  layout=ARFUSE_LAYOUT_PLAIN, fp8_out=None, status=None, reset=None, split=0,
+                  workspace=None):
     """Checked addresses of every buffer of a fused call (see _buf)."""
     plane = t * d * 2
     pbytes = 2 * plane if layout == ARFUSE_LAYOUT_LL else plane
@@ -153,6 +159,7 @@ def _call_buffers(partials, residual, gamma, out, residual_out, fp4_out, fp4_sca
         fp4_scales=_buf(fp4_scales, t * d // 16, "fp4_scales"),
         fp8_out=_buf(fp8_out, t * d, "fp8_out"),
         status=_buf(status, 16, "status"),
+        workspace=_buf(workspace, 16 * t * max(1, int(split)), "workspace"),
         reset=None if reset is None else [_buf(r, plane, "reset[%d]" % i)
                                           for i, r in enumerate(reset)])
 
@@ -167,7 +174,8 @@ def _stream(stream) -> int:
 
 
 def _opts(layout=ARFUSE_LAYOUT_PLAIN, ll_flag=0, max_polls=0, status=None, block_threads=0,
-          vpt=0, sentinel=0, reset=None, fp8_out=None, fp8_inv_scale=1.0):
+          vpt=0, sentinel=0, reset=None, fp8_out=None, fp8_inv_scale=1.0, split=0,
+          workspace=None):
     """Build an arfuse_opts; returns (opts, keepalive) - the host array of
     reset pointers must outlive the call."""
     keep = None
@@ -177,8 +185,9 @@ def _opts(layout=ARFUSE_LAYOUT_PLAIN, ll_flag=0, max_polls=0, status=None, block
         reset_addr = ctypes.addressof(keep)
     o = arfuse_opts(layout=int(layout), max_polls=int(max_polls), ll_flag=int(ll_flag),
                     status=_addr(status), block_threads=int(block_threads), vpt=int(vpt),
-                    sentinel=int(sentinel), reserved=0, reset=reset_addr,
-                    fp8_out=_addr(fp8_out), fp8_inv_scale=float(fp8_inv_scale), reserved2=0)
+                    sentinel=int(sentinel), split=int(split), reset=reset_addr,
+                    fp8_out=_addr(fp8_out), fp8_inv_scale=float(fp8_inv_scale), reserved2=0,
+                    workspace=_addr(workspace))
     o._keep = keep
     return o
 
@@ -212,15 +221,18 @@ def arfuse_rmsnorm_ex(partials: Sequence, residual, gamma, eps: float, out, resi
                       fp4_out=None, fp4_scales=None, stream=None, t=None, d=None, *,
                       layout=ARFUSE_LAYOUT_PLAIN, ll_flag=0, max_polls=0, status=None,
                       block_threads=0, vpt=0, sentinel=0, reset=None, fp8_out=None,
-                      fp8_inv_scale=1.0) -> None:
+                      fp8_inv_scale=1.0, split=0, workspace=None) -> None:
     """Fused call with options; see arfuse_rmsnorm_ex in include/arfuse.h.
     residual and gamma may be None (the no-residual and all-reduce-only
-    patterns); then pass t and d explicitly."""
+    patterns); then pass t and d explicitly. split > 1 divides each row
+    between that many workgroups, which exchange their sums of squares
+    through `workspace` (t * split 16-byte slots, zeroed before first use)."""
     t, d = _td(residual, t, d)
     b = _call_buffers(partials, residual, gamma, out, residual_out, fp4_out, fp4_scales, t, d,
-                      layout=layout, fp8_out=fp8_out, status=status, reset=reset)
+                      layout=layout, fp8_out=fp8_out, status=status, reset=reset, split=split,
+                      workspace=workspace)
     o = _opts(layout, ll_flag, max_polls, b["status"], block_threads, vpt, sentinel, b["reset"],
-              b["fp8_out"], fp8_inv_scale)
+              b["fp8_out"], fp8_inv_scale, split, b["workspace"])
     rc = lib.arfuse_rmsnorm_ex(b["arr"], len(partials), b["residual"], b["gamma"], float(eps),
                                b["out"], b["residual_out"], b["fp4_out"], b["fp4_scales"],
                                t, d, _stream(stream), ctypes.byref(o))

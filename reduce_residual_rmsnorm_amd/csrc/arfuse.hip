@@ -161,6 +161,20 @@ int64_t reset_blocks(int n, int64_t t, int64_t d, int block, bool reset) {
   return (int64_t)n * ((plane_vecs + block - 1) / block);
 }
 
+// Split rows: the validated number of workgroups per row, as its log2 (0 when
+// a row is one workgroup). Every workgroup of a split row must be resident at
+// once, hence the cap on t * split.
+int split_log2(const arfuse_opts* o, int64_t t, int64_t d, int* lg) {
+  const uint32_t s = o ? o->split : 0u;
+  *lg = 0;
+  if (s <= 1) return ARFUSE_OK;
+  if (s != 2 && s != 4 && s != 8) return ARFUSE_ERR_INVALID_ARG;
+  if (d % (16 * (int64_t)s)) return ARFUSE_ERR_INVALID_ARG;
+  if (t * (int64_t)s > ARFUSE_MAX_SPLIT_BLOCKS) return ARFUSE_ERR_UNSUPPORTED;
+  *lg = s == 2 ? 1 : s == 4 ? 2 : 3;
+  return ARFUSE_OK;
+}
+
 int check_shape(int n, int64_t t, int64_t d, int epi) {
   if (n < 1 || n > ARFUSE_MAX_PARTIALS) return ARFUSE_ERR_INVALID_ARG;
   if (t < 0 || d <= 0 || d % 16) return ARFUSE_ERR_INVALID_ARG;
@@ -178,7 +192,7 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
   if (layout != ARFUSE_LAYOUT_PLAIN && layout != ARFUSE_LAYOUT_LL &&
       layout != ARFUSE_LAYOUT_SENTINEL)
     return ARFUSE_ERR_INVALID_ARG;
-  if (opts && (opts->reserved != 0 || opts->reserved2 != 0)) return ARFUSE_ERR_INVALID_ARG;
+  if (opts && opts->reserved2 != 0) return ARFUSE_ERR_INVALID_ARG;
   if (opts && opts->max_polls > ARFUSE_MAX_POLLS) return ARFUSE_ERR_INVALID_ARG;
   const bool ll = layout == ARFUSE_LAYOUT_LL;
   const bool sentinel = layout == ARFUSE_LAYOUT_SENTINEL;
@@ -193,10 +207,17 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
   int rc = check_shape(n, t, d, epi);
   if (rc) return rc;
   if (!(eps >= 0.0f) || !isfinite(eps)) return ARFUSE_ERR_INVALID_ARG;
+  int lg = 0;
+  rc = split_log2(opts, t, d, &lg);
+  if (rc) return rc;
   int block = 0, vpt = 0;
-  rc = choose_launch(d / 8, opts, &block, &vpt);
+  rc = choose_launch((d / 8) >> lg, opts, &block, &vpt);
   if (rc) return rc;
   if (t == 0) return ARFUSE_OK;  // no-op: buffers are never touched, may be NULL
+  // the split exchange (sums of squares) needs the workspace; the all-reduce
+  // alone has no norm and splits without one
+  void* workspace = (opts && lg != 0 && epi != 0) ? opts->workspace : nullptr;
+  if (lg != 0 && epi != 0 && (!workspace || !aligned16(workspace))) return ARFUSE_ERR_INVALID_ARG;
   if (!partials) return ARFUSE_ERR_INVALID_ARG;
   if ((fp4_out == nullptr) != (fp4_scales == nullptr)) return ARFUSE_ERR_INVALID_ARG;
   if (epi != 0 && !gamma) return ARFUSE_ERR_INVALID_ARG;  // norm outputs need gamma
@@ -214,7 +235,7 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
     in[nin++] = range_of(partials[i], pbytes);
   }
   if (gamma && epi != 0) in[nin++] = range_of(gamma, d * 4);
-  Range outs[5 + ARFUSE_MAX_PARTIALS];
+  Range outs[6 + ARFUSE_MAX_PARTIALS];
   int nout = 0;
   const bool rout_first = residual_out != nullptr;
   if (residual_out) outs[nout++] = range_of(residual_out, plane);
@@ -224,6 +245,7 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
     outs[nout++] = range_of(fp4_scales, t * d / 16);
   }
   if (fp8_out) outs[nout++] = range_of(fp8_out, t * d);
+  if (workspace) outs[nout++] = range_of(workspace, (t << lg) * 16);
   if (reset) {
     for (int i = 0; i < n; ++i) {
       if (!reset[i] || !aligned16(reset[i])) return ARFUSE_ERR_INVALID_ARG;
@@ -268,13 +290,16 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
   a.flags = (residual ? kHasResidual : 0u) | (residual_out ? kHasResidualOut : 0u) |
             ((reset && extra == 0) ? kReset : 0u);
   a.rows = (uint32_t)t;
+  a.split_log2 = (uint32_t)lg;
+  a.ds8 = (uint32_t)((d / 8) >> lg);
+  a.ws = (u32x4*)workspace;
   a.plane_vecs = (uint32_t)(t * d / 8);  // only read by reset blocks: t <= 128
   a.reset_bpp = (uint32_t)((t * d / 8 + block - 1) / block);
 
   const void* fn = (const void*)select_row_kernel(n, vpt, layout, epi);
   if (!fn) return ARFUSE_ERR_UNSUPPORTED;
   void* args[] = {&a};
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(t + extra)), dim3((unsigned)block), args, 0,
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)((t << lg) + extra)), dim3((unsigned)block), args, 0,
                                  (hipStream_t)stream);
   return launch_status(e);
 }
@@ -330,13 +355,19 @@ int arfuse_query_launch(int n_partials, int64_t t, int64_t d, int epilogue,
   if (opts && opts->layout != ARFUSE_LAYOUT_PLAIN && opts->layout != ARFUSE_LAYOUT_LL &&
       opts->layout != ARFUSE_LAYOUT_SENTINEL)
     return ARFUSE_ERR_INVALID_ARG;
+  int lg = 0;
+  rc = split_log2(opts, t, d, &lg);
+  if (rc) return rc;
   int block = 0, vpt = 0;
-  rc = choose_launch(d / 8, opts, &block, &vpt);
+  rc = choose_launch((d / 8) >> lg, opts, &block, &vpt);
   if (rc) return rc;
   const bool reset = opts && opts->layout == ARFUSE_LAYOUT_SENTINEL && opts->reset;
-  info->grid = t + reset_blocks(n_partials, t, d, block, reset);
+  info->grid = (t << lg) + reset_blocks(n_partials, t, d, block, reset);
   info->block = block;
   info->vpt = vpt;
+  info->split = 1 << lg;
+  info->reserved = 0;
+  info->workspace_bytes = lg ? (t << lg) * 16 : 0;
   return ARFUSE_OK;
 }
 
@@ -344,12 +375,15 @@ int arfuse_launch_floor(int n_partials, int64_t t, int64_t d, int epilogue,
                         const arfuse_opts* opts, void* stream) {
   int rc = check_shape(n_partials, t, d, epilogue);
   if (rc) return rc;
+  int lg = 0;
+  rc = split_log2(opts, t, d, &lg);
+  if (rc) return rc;
   int block = 0, vpt = 0;
-  rc = choose_launch(d / 8, opts, &block, &vpt);
+  rc = choose_launch((d / 8) >> lg, opts, &block, &vpt);
   if (rc) return rc;
   if (t == 0) return ARFUSE_OK;
   const bool reset = opts && opts->layout == ARFUSE_LAYOUT_SENTINEL && opts->reset;
-  const int64_t grid = t + reset_blocks(n_partials, t, d, block, reset);
+  const int64_t grid = (t << lg) + reset_blocks(n_partials, t, d, block, reset);
   RowArgs a = {};
   void* args[] = {&a};
   hipError_t e = hipLaunchKernel((const void*)floor_kernel, dim3((unsigned)grid), dim3((unsigned)block),

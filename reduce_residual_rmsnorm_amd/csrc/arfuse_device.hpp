@@ -43,6 +43,12 @@ struct RowArgs {
   uint32_t rows;        // t
   uint32_t plane_vecs;  // 16-byte vectors per slot plane (t * d / 8)
   uint32_t reset_bpp;   // reset blocks per plane (plane_vecs / block, rounded up)
+  // split rows: workgroup b < rows << split_log2 takes column slice
+  // b & (split - 1) of row b >> split_log2; the slice's workgroups exchange
+  // their sums of squares through ws (slot b: {fp64 partial, sequence, 0})
+  uint32_t split_log2;  // 0: one workgroup per row
+  uint32_t ds8;         // 16-byte vectors per slice (d8 >> split_log2)
+  u32x4* ws;
 };
 
 // RowArgs.flags. These features do not change the kernel's shape, so they are
@@ -180,6 +186,11 @@ __device__ __forceinline__ bool ll_ok(u32x4 w, uint64_t flag) {
   return (w.z == (uint32_t)flag) & (w.w == (uint32_t)(flag >> 32));
 }
 
+// Store of a 16-byte word that workgroups on other CUs poll: written through
+// the caches (sc0 sc1, the same policy as reread16), one instruction, so a
+// reader sees either the old word or all of the new one.
+__device__ __forceinline__ void store16_through(char* base, uint32_t bytes, uint32_t off, u32x4 v);
+
 // Re-read of a 16-byte vector another agent may still be writing: a buffer
 // load through a descriptor of the row (scalar registers) at the lane's
 // 32-bit offset, bypassing the caches (sc0 sc1) and kept in the polling loop
@@ -194,6 +205,15 @@ __device__ __forceinline__ u32x4 reread16(const char* row, uint32_t row_bytes, u
       __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, (int)row_bytes, kBufferWord3);
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kRereadPolicy);
 }
+
+__device__ __forceinline__ void store16_through(char* base, uint32_t bytes, uint32_t off, u32x4 v) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, kBufferWord3);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kRereadPolicy);
+}
+
+// Split rows: bounded wait for a partner's slot (about a quarter second).
+constexpr uint32_t kExchangePolls = 1u << 18;
 
 // A word whose flag does not match is re-read, a short sleep apart, at most
 // max_polls times. Returns the last word read; *bad counts a word that never
@@ -387,22 +407,34 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   constexpr bool G_AFTER_ARRIVAL = NORM && ALL_AT_ONCE && SENT;
   const int lane = threadIdx.x;
   const int nthr = blockDim.x;
+  const uint32_t lg = a.split_log2;
+  const uint32_t row_blocks = a.rows << lg;
   if constexpr (SENT) {
     // a reset block (only launched when the rows are few): refill one chunk
     // of one slot plane of the set a later call reuses, a vector per lane,
     // on a CU that no row occupies
-    if (blockIdx.x >= a.rows) {
-      const uint32_t b = blockIdx.x - a.rows;
+    if (blockIdx.x >= row_blocks) {
+      const uint32_t b = blockIdx.x - row_blocks;
       const uint32_t i = b / a.reset_bpp;
       const uint32_t v = (b - i * a.reset_bpp) * (uint32_t)nthr + (uint32_t)lane;
       if (v < a.plane_vecs) store16(a.reset[i] + v, u32x4{a.sentinel2, a.sentinel2, a.sentinel2, a.sentinel2});
       return;
     }
   }
-  const uint32_t d = (uint32_t)(a.d8 * 8);
-  const int64_t rb = (int64_t)blockIdx.x * d;  // first element of the row
+  // this workgroup's columns: the whole row, or one slice of a split row
+  const uint32_t row = blockIdx.x >> lg;
+  const uint32_t slice = blockIdx.x & ((1u << lg) - 1u);
+  const uint32_t d = (uint32_t)(a.d8 * 8);  // the row width: the mean's divisor
+  const uint32_t ds = a.ds8 * 8;            // the columns this workgroup handles
+  const int64_t rb = (int64_t)row * d + (int64_t)slice * ds;  // its first element
   const bool has_res = (a.flags & kHasResidual) != 0;
   const bool has_rout = (a.flags & kHasResidualOut) != 0;
+  // split rows: this workgroup's slot sequence from the previous call, read
+  // now so the load overlaps the row's
+  uint32_t own_seq = 0;
+  if constexpr (NORM) {
+    if (lg != 0 && lane == 0) own_seq = reread16((const char*)a.ws, row_blocks * 16, blockIdx.x * 16).z;
+  }
 
   // row bases: partials (bf16, or LL words of 4 bytes per element), residual,
   // outputs (bf16), FP4 codes (half a byte per element), scales (1/16), FP8
@@ -410,7 +442,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
 #pragma unroll
   for (int i = 0; i < N; ++i) prow[i] = (const char*)a.part[i] + rb * (LL ? 4 : 2);
   const char* rrow = (const char*)a.residual + rb * 2;
-  const char* grow = (const char*)a.gamma;
+  const char* grow = (const char*)a.gamma + (int64_t)slice * ds * 4;
   char* orow = (char*)a.residual_out + rb * 2;
   char* yrow = (char*)a.out + rb * 2;
   char* crow = (char*)a.codes + rb / 2;
@@ -426,13 +458,13 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const uint32_t e = (uint32_t)group_elem<LL>(k, j, ln, nthr);
-        ok[k][j] = e < d;
-        eo[k][j] = ok[k][j] ? e : d - 4;
+        ok[k][j] = e < ds;
+        eo[k][j] = ok[k][j] ? e : ds - 4;
       }
     } else {  // the two groups of a plain vector share one validity
       const uint32_t e = (uint32_t)group_elem<LL>(k, 0, ln, nthr);
-      ok[k][0] = ok[k][1] = e < d;
-      eo[k][0] = ok[k][0] ? e : d - 8;
+      ok[k][0] = ok[k][1] = e < ds;
+      eo[k][0] = ok[k][0] ? e : ds - 8;
       eo[k][1] = eo[k][0] + 4;
     }
   };
@@ -506,7 +538,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             if (ok[k][j] && !ll_ok(raw[k][i][j], a.ll_flag))
-              raw[k][i][j] = ll_repoll(prow[i], d * 4, eo[k][j] * 4, raw[k][i][j], a.ll_flag,
+              raw[k][i][j] = ll_repoll(prow[i], ds * 4, eo[k][j] * 4, raw[k][i][j], a.ll_flag,
                                        a.max_polls, &bad);
       }
     } else if constexpr (SENT) {
@@ -518,7 +550,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
 #pragma unroll
         for (int i = 0; i < N; ++i)
           if (ok[k][0] && holds_sentinel(raw[k][i][0], a.sentinel2))
-            raw[k][i][0] = sentinel_repoll(prow[i], d * 2, eo[k][0] * 2, raw[k][i][0],
+            raw[k][i][0] = sentinel_repoll(prow[i], ds * 2, eo[k][0] * 2, raw[k][i][0],
                                            a.sentinel2, a.max_polls, &bad);
       }
     }
@@ -637,7 +669,52 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   __syncthreads();
   const int nw = nthr / kWave;
   const int wl = lane & (kWave - 1);
-  const double tot = lane_f64(row16_sum(wl < nw ? red[wl] : 0.0), 0);
+  double tot = lane_f64(row16_sum(wl < nw ? red[wl] : 0.0), 0);
+  if (lg != 0) {
+    // Split row: publish this slice's sum of squares with the next sequence,
+    // then lanes 0..split-1 of wave 0 wait (bounded) for every partner slot
+    // to carry it; the partials are added in slice order, so every slice
+    // computes the same total. A later sequence than expected means the
+    // workspace is out of step with the calls.
+    __shared__ double xsum;
+    if (lane < kWave) {
+      const uint32_t seq = (uint32_t)__builtin_amdgcn_readfirstlane((int)own_seq) + 1u;
+      char* wsb = (char*)a.ws;
+      const uint32_t wsbytes = row_blocks * 16;
+      if (lane == 0) {
+        const uint64_t tb = (uint64_t)__double_as_longlong(tot);
+        store16_through(wsb, wsbytes, blockIdx.x * 16, u32x4{(uint32_t)tb, (uint32_t)(tb >> 32), seq, 0u});
+      }
+      double part = tot;
+      uint32_t xbad = 0;
+      if (lane < (1 << lg) && (uint32_t)lane != slice) {
+        const uint32_t off = ((row << lg) + (uint32_t)lane) * 16;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        bool got = false;
+        for (uint32_t i = 0; i < kExchangePolls; ++i) {
+          w = reread16(wsb, wsbytes, off);
+          const int32_t ahead = (int32_t)(w.z - seq);
+          if (ahead == 0) {
+            got = true;
+            break;
+          }
+          if (ahead > 0) break;
+          if (i >= 64) __builtin_amdgcn_s_sleep(1);
+        }
+        part = got ? __hiloint2double((int)w.y, (int)w.x) : 0.0;
+        xbad = got ? 0u : 1u;
+      }
+      double sum = 0.0;
+      for (int p = 0; p < (1 << lg); ++p) sum += lane_f64(part, p);
+      if (lane == 0) xsum = sum;
+      if (xbad && a.status) {
+        atomicAdd(&a.status->exchange_timeouts, xbad);
+        atomicOr(&a.status->code, (uint32_t)ARFUSE_ERR_FLAG_TIMEOUT);
+      }
+    }
+    __syncthreads();
+    tot = xsum;
+  }
   const double inv = 1.0 / sqrt(tot / (double)d + (double)a.eps);
 
   // ---- normalize, scale by gamma, store bf16 / FP4 / FP8

@@ -37,7 +37,7 @@ def test_symbol_exported(name):
 
 
 def test_version_and_status_strings():
-    assert arf.arfuse_version() == 1
+    assert arf.arfuse_version() == 2
     for code in range(5):
         assert arf.arfuse_status_string(code)
     assert arf.arfuse_status_string(99) == "unknown status"
@@ -137,7 +137,7 @@ def test_sentinel_options_validated():
     o = arf._opts(layout=S, reset=[spaced(20 + i) for i in range(4)])
     assert call(**good(opts=o, t=0)) == arf.ARFUSE_OK
     o = arf._opts()
-    o.reserved = 1
+    o.reserved2 = 1
     assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
     # the re-read bound
     o = arf._opts(layout=S, max_polls=arf.ARFUSE_MAX_POLLS)
@@ -278,3 +278,31 @@ def test_binding_rejects_host_small_and_strided_tensors():
                               layout=arf.ARFUSE_LAYOUT_LL)
     with pytest.raises(ValueError, match="status"):
         arf.arfuse_rmsnorm_ex([ok], ok, FakeCuda(4 * d), 1e-5, ok, ok, status=FakeCuda(8))
+
+
+def test_split_options_validated():
+    """split must be 1, 2, 4 or 8, divide the row in whole FP4 blocks, keep
+    t * split within the resident cap and come with an aligned workspace that
+    overlaps no other buffer."""
+    ws = spaced(40)
+    assert call(**good(opts=arf._opts(split=4, workspace=ws), t=0)) == arf.ARFUSE_OK
+    for bad_split in (3, 16):
+        assert call(**good(opts=arf._opts(split=bad_split, workspace=ws))) == arf.ARFUSE_ERR_INVALID_ARG
+    # 4112 = 16 * 257: whole FP4 blocks per slice only without a split
+    assert call(**good(opts=arf._opts(split=2, workspace=ws), d=4112)) == arf.ARFUSE_ERR_INVALID_ARG
+    assert call(**good(opts=arf._opts(split=4))) == arf.ARFUSE_ERR_INVALID_ARG  # no workspace
+    assert call(**good(opts=arf._opts(split=4, workspace=ws + 8))) == arf.ARFUSE_ERR_INVALID_ARG
+    assert call(**good(opts=arf._opts(split=8, workspace=ws), t=33)) == arf.ARFUSE_ERR_UNSUPPORTED
+    # the workspace is written: it may overlap neither a partial nor an output
+    assert call(**good(opts=arf._opts(split=2, workspace=spaced(0)))) == arf.ARFUSE_ERR_INVALID_ARG
+    assert call(**good(opts=arf._opts(split=2, workspace=spaced(11) + 16))) == arf.ARFUSE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("t,d,split,block,grid", [(8, 8192, 4, 256, 32), (8, 8192, 2, 512, 16),
+                                                 (1, 4096, 8, 64, 8), (64, 8192, 4, 256, 256)])
+def test_query_launch_split(t, d, split, block, grid):
+    info = arf.arfuse_query_launch(8, t, d, split=split)
+    assert (info.grid, info.block, info.vpt, info.split) == (grid, block, 1, split)
+    assert info.workspace_bytes == 16 * t * split
+    plain = arf.arfuse_query_launch(8, t, d)
+    assert (plain.split, plain.workspace_bytes, plain.grid) == (1, 0, t)

@@ -1,0 +1,270 @@
+"""Split rows against the oracle on the GPU.
+
+A row's columns are divided among 2, 4 or 8 workgroups. Each sums the squares
+of its slice, publishes the share with the next sequence number in its slot of
+a caller-zeroed workspace and waits, bounded, for the row's other shares; all
+of them add the shares in slice order. This is a re-layout of the row
+reduction the fused operator does inside one workgroup (Deep Dive: AllReduce
+and AllReduce Fusion in TensorRT-LLM, §6.3 and §6.5: RMSNorm over the whole
+hidden dimension), so the outputs meet the same bar as the unsplit call:
+residual_out bit-exact, y, FP4 and FP8 to the oracle's tolerance."""
+
+import numpy as np
+import pytest
+import torch
+
+import reduce_residual_rmsnorm_amd as arf
+import seeded_inputs as si
+from gpu_util import (DEV, assert_fp4_close, assert_residual_exact, assert_y_close, dev_f32,
+                      dev_u8, dev_u16, host_u16, note)
+
+pytestmark = pytest.mark.gpu
+LL = arf.ARFUSE_LAYOUT_LL
+SENT = arf.ARFUSE_LAYOUT_SENTINEL
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def orc():
+    return __import__("oracle").default()
+
+
+def new_status():
+    return torch.zeros(4, dtype=torch.int32, device=DEV)
+
+
+def read_status(st):
+    """(code, exchange_timeouts, bad_words) of an arfuse_ll_status."""
+    v = st.cpu().numpy().view(np.uint32)
+    return int(v[0]), int(v[1]), int(v[2]) | (int(v[3]) << 32)
+
+
+def workspace(t, split):
+    return torch.zeros(16 * t * split, dtype=torch.uint8, device=DEV)
+
+
+def assert_fp8_close(got, want, frac=1e-4):
+    g = got.astype(np.int16)
+    w = want.astype(np.int16)
+    diff = g != w
+    if diff.any():
+        assert np.all((g[diff] & 0x80) == (w[diff] & 0x80)), "FP8 sign differs"
+        assert np.abs((g[diff] & 0x7F) - (w[diff] & 0x7F)).max() <= 1, "FP8 off by more than a step"
+    assert diff.sum() <= frac * g.size, "FP8: %d of %d codes differ" % (diff.sum(), g.size)
+
+
+class Call:
+    """Device buffers of one call; `go` enqueues it with the given options."""
+
+    def __init__(self, ci, *, layout=0, flag=None, residual=True, gamma=True, out=True,
+                 rout=True, fp4=False, fp8=None):
+        t, d = ci.t, ci.d
+        self.ci, self.layout, self.flag, self.fp8 = ci, layout, flag, fp8
+        if layout == LL:
+            self.parts = [dev_u8(si.ll_pack(p, flag)) for p in ci.partials]
+        else:
+            self.parts = [dev_u16(p) for p in ci.partials]
+        self.res = dev_u16(ci.residual) if residual else None
+        self.g = dev_f32(ci.gamma) if gamma else None
+        self.o = torch.empty((t, d), dtype=torch.bfloat16, device=DEV) if out else None
+        self.ro = torch.empty((t, d), dtype=torch.bfloat16, device=DEV) if rout else None
+        self.codes = torch.empty((t, d // 2), dtype=torch.uint8, device=DEV) if fp4 else None
+        self.scales = torch.empty((t, d // 16), dtype=torch.uint8, device=DEV) if fp4 else None
+        self.f8 = torch.empty((t, d), dtype=torch.uint8, device=DEV) if fp8 is not None else None
+
+    def go(self, **opts):
+        ci = self.ci
+        arf.arfuse_rmsnorm_ex(self.parts, self.res, self.g, float(ci.eps), self.o, self.ro,
+                              self.codes, self.scales, t=ci.t, d=ci.d, layout=self.layout,
+                              ll_flag=self.flag or 0, fp8_out=self.f8,
+                              fp8_inv_scale=self.fp8 if self.fp8 is not None else 1.0, **opts)
+
+    def fetch(self):
+        torch.cuda.synchronize()
+        return dict(residual_out=host_u16(self.ro) if self.ro is not None else None,
+                    out=host_u16(self.o) if self.o is not None else None,
+                    codes=self.codes.cpu().numpy() if self.codes is not None else None,
+                    scales=self.scales.cpu().numpy() if self.scales is not None else None,
+                    fp8=self.f8.cpu().numpy() if self.f8 is not None else None)
+
+
+def check(got, ref, rows=slice(None)):
+    if got["residual_out"] is not None:
+        assert_residual_exact(got["residual_out"][rows], ref["residual_out"][rows])
+    if got["out"] is not None:
+        assert_y_close(got["out"][rows], ref["y32"][rows], ref["out"][rows])
+    if got["codes"] is not None:
+        assert_fp4_close(got["codes"][rows], got["scales"][rows], ref["codes"][rows],
+                         ref["scales"][rows])
+    if got["fp8"] is not None:
+        assert_fp8_close(got["fp8"][rows], ref["fp8"][rows])
+
+
+def reference(ci, residual=True, gamma=True, out=True, rout=True, fp4=False, fp8=None):
+    return orc().fused(ci.partials, ci.residual if residual else None,
+                       ci.gamma if gamma else None, ci.eps, out=out, fp4=fp4,
+                       fp8_inv_scale=fp8, residual_out=rout)
+
+
+@pytest.mark.parametrize("split", [2, 4, 8])
+@pytest.mark.parametrize("layout", [0, LL, SENT])
+def test_split_matches_oracle(layout, split):
+    ci = si.make_call(8, 9, 8192, seed=200 + split + 10 * layout, outlier_frac=0.2)
+    flag = ci.ll_base + 5
+    ref = reference(ci, fp4=True)
+    c = Call(ci, layout=layout, flag=flag, fp4=True)
+    st = new_status()
+    info = arf.arfuse_query_launch(8, 9, 8192, arf.ARFUSE_EPI_BF16 | arf.ARFUSE_EPI_FP4,
+                                   split=split, layout=layout)
+    note("split %d layout %d grid %d block %d" % (split, layout, info.grid, info.block))
+    c.go(split=split, workspace=workspace(9, split), status=st, max_polls=1)
+    got = c.fetch()
+    assert read_status(st) == (0, 0, 0)
+    check(got, ref)
+
+
+# ragged slices (idle lanes in the last vector group of each slice), the
+# largest t * split, the widest row, the narrowest slice (16 elements)
+SHAPES = [(3, 5, 2080, 2, dict(fp8=0.75)), (5, 7, 4160, 4, dict(fp4=True)),
+          (2, 3, 1152, 8, dict()), (8, 32, 8192, 8, dict(fp4=True)),
+          (5, 2, 65536, 8, dict(fp8=2.0)), (1, 1, 128, 8, dict(fp4=True)),
+          (4, 64, 8192, 4, dict(fp4=True, out=False)), (7, 128, 3072, 2, dict())]
+
+
+@pytest.mark.parametrize("n,t,d,split,kw", SHAPES)
+def test_split_shapes(n, t, d, split, kw):
+    ci = si.make_call(n, t, d, seed=210 + n + split, outlier_frac=0.3)
+    ref = reference(ci, **kw)
+    c = Call(ci, **kw)
+    st = new_status()
+    info = arf.arfuse_query_launch(n, t, d, split=split)
+    note("split shape n=%d t=%d d=%d split=%d grid=%d block=%d %s"
+         % (n, t, d, split, info.grid, info.block, kw))
+    c.go(split=split, workspace=workspace(t, split), status=st)
+    got = c.fetch()
+    assert read_status(st) == (0, 0, 0)
+    check(got, ref)
+
+
+PATTERNS = {
+    "no_residual": dict(residual=False),
+    "no_residual_out": dict(rout=False),
+    "fp8_no_residual": dict(residual=False, out=False, fp8=0.25),
+    # no norm: nothing to exchange, no workspace needed
+    "allreduce_only": dict(gamma=False, out=False),
+}
+
+
+@pytest.mark.parametrize("pattern", sorted(PATTERNS))
+def test_split_patterns(pattern):
+    kw = PATTERNS[pattern]
+    ci = si.make_call(8, 9, 8192, seed=230 + len(pattern), outlier_frac=0.2)
+    ref = reference(ci, **kw)
+    c = Call(ci, **kw)
+    ws = None if pattern == "allreduce_only" else workspace(9, 4)
+    note("split pattern %s" % pattern)
+    c.go(split=4, workspace=ws)
+    check(c.fetch(), ref)
+
+
+def test_split_sentinel_pending_and_reset():
+    """Sentinel layout with split rows: a pending vector is counted once by the
+    slice that holds it, the other rows are exact, and the reset refills the
+    whole set (here by the launch's extra workgroups, t <= 128)."""
+    n, t, d, split = 4, 6, 4096, 4
+    ci = si.make_call(n, t, d, seed=240)
+    pat = arf.ARFUSE_SENTINEL_DEFAULT
+    for p in ci.partials:
+        p[p == pat] = 0
+    ci.partials[2, 3, 1030] = pat          # row 3, slice 1
+    pending = sum(orc().sentinel_pending(p, pat) for p in ci.partials)
+    assert pending == 1
+    ref = orc().allreduce_rmsnorm(ci.partials, ci.residual, ci.gamma, ci.eps)
+    c = Call(ci, layout=SENT)
+    slots = [torch.zeros((t, d), dtype=torch.int16, device=DEV) for _ in range(n)]
+    st = new_status()
+    note("split sentinel pending + reset")
+    c.go(split=split, workspace=workspace(t, split), status=st, max_polls=3, reset=slots)
+    got = c.fetch()
+    assert read_status(st) == (arf.ARFUSE_ERR_FLAG_TIMEOUT, 0, pending)
+    clean = [0, 1, 2, 4, 5]
+    check(got, ref, rows=clean)
+    for sl in slots:
+        assert np.all(sl.cpu().numpy().view(np.uint16) == pat)
+
+
+def test_split_sequence_advances_over_calls_and_graph_replays():
+    """The workspace slots carry a sequence that every call advances: eager
+    calls, a captured chain replayed several times with eager calls between
+    the replays, all on one workspace zeroed once; every call's outputs are
+    the same bits (the shares are added in a fixed order)."""
+    n, t, d, split, k = 8, 8, 8192, 4, 6
+    ci = si.make_call(n, t, d, seed=250, outlier_frac=0.01)
+    ref = reference(ci, fp4=True)
+    c = Call(ci, fp4=True)
+    ws = workspace(t, split)
+    st = new_status()
+    note("split sequence eager")
+    c.go(split=split, workspace=ws, status=st)
+    first = c.fetch()
+    check(first, ref)
+
+    def enqueue():
+        for _ in range(k):
+            c.go(split=split, workspace=ws, status=st)
+
+    gr = torch.cuda.CUDAGraph()
+    note("split sequence capture")
+    with torch.cuda.graph(gr):
+        enqueue()
+    for rep in range(3):
+        c.o.zero_()
+        c.codes.zero_()
+        torch.cuda.synchronize()
+        note("split sequence replay %d" % rep)
+        gr.replay()
+        got = c.fetch()
+        assert read_status(st) == (0, 0, 0)
+        for key in ("residual_out", "out", "codes", "scales"):
+            assert np.array_equal(got[key], first[key]), key
+        enqueue()
+        torch.cuda.synchronize()
+    seq = ws.cpu().numpy().view(np.uint32).reshape(t * split, 4)[:, 2]
+    assert np.all(seq == 1 + 2 * 3 * k), seq   # one eager call, 3 replays and 3 eager chains
+
+
+def test_split_out_of_step_workspace_reported():
+    """A slot carrying a later sequence than the call expects (a workspace out
+    of step with the calls) is reported in exchange_timeouts, the bounded wait
+    of the slot's own workgroup ends, and the other rows are exact; zeroing the
+    workspace again restores the row."""
+    n, t, d, split = 4, 3, 4096, 2
+    ci = si.make_call(n, t, d, seed=260)
+    ref = reference(ci)
+    c = Call(ci)
+    ws = workspace(t, split)
+    st = new_status()
+    note("split out-of-step: clean call")
+    c.go(split=split, workspace=ws, status=st)
+    check(c.fetch(), ref)
+    w = ws.cpu().numpy().view(np.uint32).reshape(t * split, 4).copy()
+    assert np.all(w[:, 2] == 1)
+    w[1, 2] = 101           # row 0, slice 1: ahead of the call
+    ws.copy_(torch.from_numpy(w.view(np.uint8).reshape(-1)).to(DEV))
+    note("split out-of-step: planted sequence")
+    c.go(split=split, workspace=ws, status=st)
+    got = c.fetch()
+    # slice 0 sees a later sequence (1), slice 1 never sees its own (1)
+    assert read_status(st) == (arf.ARFUSE_ERR_FLAG_TIMEOUT, 2, 0)
+    check(got, ref, rows=[1, 2])
+    assert_residual_exact(got["residual_out"], ref["residual_out"])   # not norm-dependent
+    ws.zero_()
+    st.zero_()
+    note("split out-of-step: workspace zeroed")
+    c.go(split=split, workspace=ws, status=st)
+    check(c.fetch(), ref)
+    assert read_status(st) == (0, 0, 0)
