@@ -381,6 +381,10 @@ def recorded_traffic(workload: str):
 # are one chain each.
 DECODE_PROFILED = ("decode_n8_t8_d8192_chain160", "decode_n8_t8_d8192_chain160_ll",
                    "decode_n8_t8_d8192_chain160_sentinel", "fp4_n4_t1_d8192_x100")
+# the same instances with split rows (a run of their own: split is a launch
+# argument, not an instance)
+DECODE_SPLIT_PROFILED = ("decode_n8_t8_d8192_chain160_split4", "decode_n8_t8_d8192_chain160_ll_split4",
+                         "decode_n8_t8_d8192_chain160_sentinel_split4", "fp4_n4_t1_d8192_x100_split8")
 
 PROFILE_COMMANDS = {
     "trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
@@ -395,6 +399,9 @@ PROFILE_COMMANDS = {
     "trace_decode": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
                     "-d $OUT/prof_decode -o decode -- python3 $REPO/bench.py "
                     + " ".join("--only-extra " + x for x in DECODE_PROFILED),
+    "trace_decode_split": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
+                          "-d $OUT/prof_decode_split -o decode -- python3 $REPO/bench.py "
+                          + " ".join("--only-extra " + x for x in DECODE_SPLIT_PROFILED),
 }
 
 
@@ -464,19 +471,22 @@ def summarize_profiles(outdir: str) -> None:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec, indent=1))
-    if os.path.exists(os.path.join(outdir, "prof_decode", "decode_kernel_stats.csv")):
-        summarize_decode_profile(outdir)
+    for which in ("decode", "decode_split"):
+        if os.path.exists(os.path.join(outdir, "prof_" + which, "decode_kernel_stats.csv")):
+            summarize_decode_profile(outdir, which)
 
 
-def summarize_decode_profile(outdir: str) -> None:
-    """profiles/row_kernel_decode_chains_stats.md: kernel durations of the
+def summarize_decode_profile(outdir: str, which: str = "decode") -> None:
+    """profiles/row_kernel_decode_chains_stats.md (or, for the split-row
+    chains, row_kernel_decode_split_chains_stats.md): kernel durations of the
     decode chains next to the graph's time per node."""
     import csv
-    line = _bench_line(os.path.join(outdir, "prof_decode.log")) or {}
-    rows = list(csv.DictReader(open(os.path.join(outdir, "prof_decode", "decode_kernel_stats.csv"))))
-    md = ["# row_kernel, decode chains: rocprofv3 kernel statistics", "",
+    line = _bench_line(os.path.join(outdir, "prof_%s.log" % which)) or {}
+    rows = list(csv.DictReader(open(os.path.join(outdir, "prof_" + which, "decode_kernel_stats.csv"))))
+    title = "decode chains" if which == "decode" else "decode chains with split rows"
+    md = ["# row_kernel, %s: rocprofv3 kernel statistics" % title, "",
           "Command (`$REPO` is the repository root, `$OUT` the output directory):", "",
-          "    " + PROFILE_COMMANDS["trace_decode"], "",
+          "    " + PROFILE_COMMANDS["trace_" + which], "",
           "Kernel source sha256[:16]: `%s`" % line.get("kernel_source", "?"), "",
           "Each chain is captured once in a graph and replayed (5 warm-up + 200 timed "
           "replays), then the same-length graph of the empty kernel is replayed. Every "
@@ -500,7 +510,9 @@ def summarize_decode_profile(outdir: str) -> None:
         for k, v in ex.items():
             md.append("| %s | %.2f | %.2f | %.2f |" % (k, v["us_per_call_p50"],
                                                      v["floor_us_per_node_p50"], v["ratio_to_floor"]))
-    with open(os.path.join(PROFILES, "row_kernel_decode_chains_stats.md"), "w") as f:
+    fname = "row_kernel_decode_chains_stats.md" if which == "decode" else \
+        "row_kernel_decode_split_chains_stats.md"
+    with open(os.path.join(PROFILES, fname), "w") as f:
         f.write("\n".join(md) + "\n")
 
 
@@ -542,7 +554,13 @@ def extra_table():
             (8, 8, 8192, 160, "ll_split4", False, "decode_n8_t8_d8192_chain160_ll_split4"),
             (8, 8, 8192, 160, "sentinel_split4", False, "decode_n8_t8_d8192_chain160_sentinel_split4"),
             (4, 1, 8192, 100, "split8", True, "fp4_n4_t1_d8192_x100_split8"),
-            (4, 8, 8192, 100, "split4", True, "fp4_n4_t8_d8192_x100_split4")]:
+            (4, 8, 8192, 100, "split4", True, "fp4_n4_t8_d8192_x100_split4"),
+            # shapes where one workgroup per row leaves most of each CU's time to
+            # a single row: twice the width, and 128 rows (two rows per CU)
+            (8, 8, 16384, 100, "", False, "decode_n8_t8_d16384_x100"),
+            (8, 8, 16384, 100, "split8", False, "decode_n8_t8_d16384_x100_split8"),
+            (8, 128, 8192, 50, "", False, "decode_n8_t128_d8192_x50"),
+            (8, 128, 8192, 50, "split2", False, "decode_n8_t128_d8192_x50_split2")]:
         sp = int(mode.split("split")[1]) if "split" in mode else 0
         t[label] = (lambda nn=nn, tt=tt, dd=dd, kk=kk, mode=mode, fp4=fp4, sp=sp:
                     decode_chain(nn, tt, dd, kk, ll=mode.startswith("ll"), fp4=fp4, out=not fp4,

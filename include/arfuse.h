@@ -134,6 +134,9 @@ typedef struct {
  * once for the exchange). */
 #define ARFUSE_MAX_SPLIT 8
 #define ARFUSE_MAX_SPLIT_BLOCKS 256
+/* opts->split value that lets the library choose the split for the shape
+ * (arfuse_query_launch reports the choice and the workspace it needs). */
+#define ARFUSE_SPLIT_AUTO 0xFFFFFFFFu
 
 /* Options of arfuse_rmsnorm_ex. Zero-initialise it for the defaults
  * (plain layout, library-chosen launch). */
@@ -158,7 +161,16 @@ typedef struct {
                                  (decode shapes, where a row is bound by one
                                  CU's issue rate). Needs workspace,
                                  d % (16 * split) == 0 and
-                                 t * split <= ARFUSE_MAX_SPLIT_BLOCKS */
+                                 t * split <= ARFUSE_MAX_SPLIT_BLOCKS; a
+                                 slice of more than 16,384 elements (or a vpt
+                                 override above 2) is ARFUSE_ERR_UNSUPPORTED.
+                                 ARFUSE_SPLIT_AUTO: the smallest split whose
+                                 slices take at most 256 threads and 32 KiB
+                                 of partial reads per workgroup, used where
+                                 it removes at least two waves per SIMD or
+                                 divides the row at least four ways, else 1;
+                                 a pure function of (n_partials, t, d,
+                                 layout) */
   void* const* reset;         /* SENTINEL: (host) array of n_partials (device)
                                  bf16 [t][d] buffers, 16-byte aligned, that this
                                  call fills with the sentinel (the slot set a
@@ -188,7 +200,8 @@ typedef struct {
                            the blocks that write the reset */
   int32_t block;        /* threads per workgroup */
   int32_t vpt;          /* 16-byte vectors per thread per partial */
-  int32_t split;        /* workgroups per row (1 unless opts->split > 1) */
+  int32_t split;        /* workgroups per row (1 unless opts->split > 1,
+                           the choice for ARFUSE_SPLIT_AUTO) */
   int32_t reserved;
   int64_t workspace_bytes; /* bytes of opts->workspace a split call needs */
 } arfuse_launch_info;

@@ -32,6 +32,7 @@ ARFUSE_MAX_D = 65536
 ARFUSE_MAX_POLLS = 1 << 20
 ARFUSE_MAX_SPLIT = 8
 ARFUSE_MAX_SPLIT_BLOCKS = 256
+ARFUSE_SPLIT_AUTO = 0xFFFFFFFF
 
 # The exported functions, as declared in include/arfuse.h.
 EXPORTED = ("arfuse_rmsnorm", "arfuse_rmsnorm_ex", "arfuse_quantize_fp4", "arfuse_query_launch",
@@ -226,10 +227,19 @@ def arfuse_rmsnorm_ex(partials: Sequence, residual, gamma, eps: float, out, resi
     residual and gamma may be None (the no-residual and all-reduce-only
     patterns); then pass t and d explicitly. split > 1 divides each row
     between that many workgroups, which exchange their sums of squares
-    through `workspace` (t * split 16-byte slots, zeroed before first use)."""
+    through `workspace` (t * split 16-byte slots, zeroed before first use);
+    ARFUSE_SPLIT_AUTO lets the library choose (arfuse_query_launch tells
+    the choice and the workspace size)."""
     t, d = _td(residual, t, d)
+    ws_split = int(split)
+    if ws_split == ARFUSE_SPLIT_AUTO:   # the workspace the library's choice needs
+        info = arfuse_launch_info()
+        q = _opts(layout=layout, split=split)
+        ws_split = (info.split if lib.arfuse_query_launch(len(partials), t, d, ARFUSE_EPI_BF16,
+                                                          ctypes.byref(q), ctypes.byref(info)) == 0
+                    else 1)
     b = _call_buffers(partials, residual, gamma, out, residual_out, fp4_out, fp4_scales, t, d,
-                      layout=layout, fp8_out=fp8_out, status=status, reset=reset, split=split,
+                      layout=layout, fp8_out=fp8_out, status=status, reset=reset, split=ws_split,
                       workspace=workspace)
     o = _opts(layout, ll_flag, max_polls, b["status"], block_threads, vpt, sentinel, b["reset"],
               b["fp8_out"], fp8_inv_scale, split, b["workspace"])

@@ -85,16 +85,16 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* src, u32x4* dst,
 
 // ------------------------------------------------------------ dispatch
 
-RowFn select_row_kernel(int n, int vpt, int layout, int epi) {
+RowFn select_row_kernel(int n, int vpt, int layout, int epi, bool split) {
   switch (n) {
-    case 1: return select_row_kernel_n1(vpt, layout, epi);
-    case 2: return select_row_kernel_n2(vpt, layout, epi);
-    case 3: return select_row_kernel_n3(vpt, layout, epi);
-    case 4: return select_row_kernel_n4(vpt, layout, epi);
-    case 5: return select_row_kernel_n5(vpt, layout, epi);
-    case 6: return select_row_kernel_n6(vpt, layout, epi);
-    case 7: return select_row_kernel_n7(vpt, layout, epi);
-    case 8: return select_row_kernel_n8(vpt, layout, epi);
+    case 1: return select_row_kernel_n1(vpt, layout, epi, split);
+    case 2: return select_row_kernel_n2(vpt, layout, epi, split);
+    case 3: return select_row_kernel_n3(vpt, layout, epi, split);
+    case 4: return select_row_kernel_n4(vpt, layout, epi, split);
+    case 5: return select_row_kernel_n5(vpt, layout, epi, split);
+    case 6: return select_row_kernel_n6(vpt, layout, epi, split);
+    case 7: return select_row_kernel_n7(vpt, layout, epi, split);
+    case 8: return select_row_kernel_n8(vpt, layout, epi, split);
   }
   return nullptr;
 }
@@ -161,12 +161,54 @@ int64_t reset_blocks(int n, int64_t t, int64_t d, int block, bool reset) {
   return (int64_t)n * ((plane_vecs + block - 1) / block);
 }
 
+// Split rows are compiled for one or two vectors per thread: a slice covers at
+// most 2 * kMaxBlock vectors (16,384 elements).
+constexpr int kMaxSplitVpt = 2;
+
+// The launch of a call whose rows are split 1 << lg ways.
+int row_launch(int64_t d, int lg, const arfuse_opts* o, int* block, int* vpt) {
+  const int rc = choose_launch((d / 8) >> lg, o, block, vpt);
+  if (rc) return rc;
+  if (lg != 0 && *vpt > kMaxSplitVpt) return ARFUSE_ERR_UNSUPPORTED;
+  return ARFUSE_OK;
+}
+
+// Work per SIMD of a workgroup covering `vecs` 16-byte vectors per partial at
+// the default launch: vectors per thread times waves per SIMD.
+int64_t work_per_simd(int64_t vecs) {
+  int64_t v = 1;
+  while (v * kMaxBlock < vecs) v *= 2;
+  const int64_t block = (vecs + v - 1) / v;
+  return v * ((block + 4 * kWave - 1) / (4 * kWave));
+}
+
+// ARFUSE_SPLIT_AUTO: the smallest split whose slices need at most 256 threads
+// (one wave per SIMD at one vector per thread) and read at most 32 KiB of
+// partials per workgroup, within the split limits; kept only where it removes
+// at least two waves' work per SIMD or divides the row four or more ways
+// (measured on MI355X decode chains: an exchange costs about 0.5 us, a wave
+// per SIMD about 0.35 us, and per-CU bytes dominate the LL layout).
+int auto_split_log2(int n, int64_t t, int64_t d, bool ll) {
+  const int64_t d8 = d / 8;
+  const int64_t vec_bytes = (ll ? 32 : 16) * (int64_t)n;
+  int lg = 0;
+  while (lg < 3 && ((d8 >> lg) > 256 || (d8 >> lg) * vec_bytes > 32768)) ++lg;
+  while (lg > 0 && ((t << lg) > ARFUSE_MAX_SPLIT_BLOCKS || d % (16LL << lg))) --lg;
+  if (lg == 0 || (d8 >> lg) > kMaxSplitVpt * kMaxBlock) return 0;
+  if (lg < 2 && work_per_simd(d8) - work_per_simd(d8 >> lg) < 2) return 0;
+  return lg;
+}
+
 // Split rows: the validated number of workgroups per row, as its log2 (0 when
 // a row is one workgroup). Every workgroup of a split row must be resident at
 // once, hence the cap on t * split.
-int split_log2(const arfuse_opts* o, int64_t t, int64_t d, int* lg) {
+int split_log2(const arfuse_opts* o, int n, int64_t t, int64_t d, int* lg) {
   const uint32_t s = o ? o->split : 0u;
   *lg = 0;
+  if (s == ARFUSE_SPLIT_AUTO) {
+    *lg = auto_split_log2(n, t, d, o->layout == ARFUSE_LAYOUT_LL);
+    return ARFUSE_OK;
+  }
   if (s <= 1) return ARFUSE_OK;
   if (s != 2 && s != 4 && s != 8) return ARFUSE_ERR_INVALID_ARG;
   if (d % (16 * (int64_t)s)) return ARFUSE_ERR_INVALID_ARG;
@@ -208,10 +250,10 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
   if (rc) return rc;
   if (!(eps >= 0.0f) || !isfinite(eps)) return ARFUSE_ERR_INVALID_ARG;
   int lg = 0;
-  rc = split_log2(opts, t, d, &lg);
+  rc = split_log2(opts, n, t, d, &lg);
   if (rc) return rc;
   int block = 0, vpt = 0;
-  rc = choose_launch((d / 8) >> lg, opts, &block, &vpt);
+  rc = row_launch(d, lg, opts, &block, &vpt);
   if (rc) return rc;
   if (t == 0) return ARFUSE_OK;  // no-op: buffers are never touched, may be NULL
   // the split exchange (sums of squares) needs the workspace; the all-reduce
@@ -296,7 +338,7 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
   a.plane_vecs = (uint32_t)(t * d / 8);  // only read by reset blocks: t <= 128
   a.reset_bpp = (uint32_t)((t * d / 8 + block - 1) / block);
 
-  const void* fn = (const void*)select_row_kernel(n, vpt, layout, epi);
+  const void* fn = (const void*)select_row_kernel(n, vpt, layout, epi, lg != 0);
   if (!fn) return ARFUSE_ERR_UNSUPPORTED;
   void* args[] = {&a};
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)((t << lg) + extra)), dim3((unsigned)block), args, 0,
@@ -356,10 +398,10 @@ int arfuse_query_launch(int n_partials, int64_t t, int64_t d, int epilogue,
       opts->layout != ARFUSE_LAYOUT_SENTINEL)
     return ARFUSE_ERR_INVALID_ARG;
   int lg = 0;
-  rc = split_log2(opts, t, d, &lg);
+  rc = split_log2(opts, n_partials, t, d, &lg);
   if (rc) return rc;
   int block = 0, vpt = 0;
-  rc = choose_launch((d / 8) >> lg, opts, &block, &vpt);
+  rc = row_launch(d, lg, opts, &block, &vpt);
   if (rc) return rc;
   const bool reset = opts && opts->layout == ARFUSE_LAYOUT_SENTINEL && opts->reset;
   info->grid = (t << lg) + reset_blocks(n_partials, t, d, block, reset);
@@ -376,10 +418,10 @@ int arfuse_launch_floor(int n_partials, int64_t t, int64_t d, int epilogue,
   int rc = check_shape(n_partials, t, d, epilogue);
   if (rc) return rc;
   int lg = 0;
-  rc = split_log2(opts, t, d, &lg);
+  rc = split_log2(opts, n_partials, t, d, &lg);
   if (rc) return rc;
   int block = 0, vpt = 0;
-  rc = choose_launch((d / 8) >> lg, opts, &block, &vpt);
+  rc = row_launch(d, lg, opts, &block, &vpt);
   if (rc) return rc;
   if (t == 0) return ARFUSE_OK;
   const bool reset = opts && opts->layout == ARFUSE_LAYOUT_SENTINEL && opts->reset;

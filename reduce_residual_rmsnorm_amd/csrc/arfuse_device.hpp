@@ -391,7 +391,7 @@ constexpr int pipeline_depth() {
   return 1;
 }
 
-template <int N, int VPT, bool LL, bool SENT, int EPI>
+template <int N, int VPT, bool LL, bool SENT, int EPI, bool SPLIT>
 __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   constexpr bool NORM = EPI != 0;
   constexpr bool OUT = (EPI & ARFUSE_EPI_BF16) != 0;
@@ -407,7 +407,9 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   constexpr bool G_AFTER_ARRIVAL = NORM && ALL_AT_ONCE && SENT;
   const int lane = threadIdx.x;
   const int nthr = blockDim.x;
-  const uint32_t lg = a.split_log2;
+  // split instances are launched with split_log2 >= 1; the others fold every
+  // slice computation away
+  const uint32_t lg = SPLIT ? a.split_log2 : 0u;
   const uint32_t row_blocks = a.rows << lg;
   if constexpr (SENT) {
     // a reset block (only launched when the rows are few): refill one chunk
@@ -425,15 +427,15 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   const uint32_t row = blockIdx.x >> lg;
   const uint32_t slice = blockIdx.x & ((1u << lg) - 1u);
   const uint32_t d = (uint32_t)(a.d8 * 8);  // the row width: the mean's divisor
-  const uint32_t ds = a.ds8 * 8;            // the columns this workgroup handles
+  const uint32_t ds = SPLIT ? a.ds8 * 8 : d;  // the columns this workgroup handles
   const int64_t rb = (int64_t)row * d + (int64_t)slice * ds;  // its first element
   const bool has_res = (a.flags & kHasResidual) != 0;
   const bool has_rout = (a.flags & kHasResidualOut) != 0;
   // split rows: this workgroup's slot sequence from the previous call, read
   // now so the load overlaps the row's
   uint32_t own_seq = 0;
-  if constexpr (NORM) {
-    if (lg != 0 && lane == 0) own_seq = reread16((const char*)a.ws, row_blocks * 16, blockIdx.x * 16).z;
+  if constexpr (NORM && SPLIT) {
+    if (lane == 0) own_seq = reread16((const char*)a.ws, row_blocks * 16, blockIdx.x * 16).z;
   }
 
   // row bases: partials (bf16, or LL words of 4 bytes per element), residual,
@@ -670,7 +672,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   const int nw = nthr / kWave;
   const int wl = lane & (kWave - 1);
   double tot = lane_f64(row16_sum(wl < nw ? red[wl] : 0.0), 0);
-  if (lg != 0) {
+  if constexpr (SPLIT) {
     // Split row: publish this slice's sum of squares with the next sequence,
     // then lanes 0..split-1 of wave 0 wait (bounded) for every partner slot
     // to carry it; the partials are added in slice order, so every slice
@@ -785,13 +787,13 @@ typedef void (*RowFn)(RowArgs);
 
 // Instances for one rank count: returns the kernel for (VPT, layout, EPI);
 // layout is ARFUSE_LAYOUT_PLAIN, _LL or _SENTINEL.
-RowFn select_row_kernel_n1(int vpt, int layout, int epi);
-RowFn select_row_kernel_n2(int vpt, int layout, int epi);
-RowFn select_row_kernel_n3(int vpt, int layout, int epi);
-RowFn select_row_kernel_n4(int vpt, int layout, int epi);
-RowFn select_row_kernel_n5(int vpt, int layout, int epi);
-RowFn select_row_kernel_n6(int vpt, int layout, int epi);
-RowFn select_row_kernel_n7(int vpt, int layout, int epi);
-RowFn select_row_kernel_n8(int vpt, int layout, int epi);
+RowFn select_row_kernel_n1(int vpt, int layout, int epi, bool split);
+RowFn select_row_kernel_n2(int vpt, int layout, int epi, bool split);
+RowFn select_row_kernel_n3(int vpt, int layout, int epi, bool split);
+RowFn select_row_kernel_n4(int vpt, int layout, int epi, bool split);
+RowFn select_row_kernel_n5(int vpt, int layout, int epi, bool split);
+RowFn select_row_kernel_n6(int vpt, int layout, int epi, bool split);
+RowFn select_row_kernel_n7(int vpt, int layout, int epi, bool split);
+RowFn select_row_kernel_n8(int vpt, int layout, int epi, bool split);
 
 }  // namespace arfuse_detail

@@ -293,6 +293,9 @@ def test_split_options_validated():
     assert call(**good(opts=arf._opts(split=4))) == arf.ARFUSE_ERR_INVALID_ARG  # no workspace
     assert call(**good(opts=arf._opts(split=4, workspace=ws + 8))) == arf.ARFUSE_ERR_INVALID_ARG
     assert call(**good(opts=arf._opts(split=8, workspace=ws), t=33)) == arf.ARFUSE_ERR_UNSUPPORTED
+    # slices wider than 16,384 elements, or more than 2 vectors per thread
+    assert call(**good(opts=arf._opts(split=2, workspace=ws), d=65536, t=1)) == arf.ARFUSE_ERR_UNSUPPORTED
+    assert call(**good(opts=arf._opts(split=4, vpt=4, workspace=ws), d=8192)) == arf.ARFUSE_ERR_UNSUPPORTED
     # the workspace is written: it may overlap neither a partial nor an output
     assert call(**good(opts=arf._opts(split=2, workspace=spaced(0)))) == arf.ARFUSE_ERR_INVALID_ARG
     assert call(**good(opts=arf._opts(split=2, workspace=spaced(11) + 16))) == arf.ARFUSE_ERR_INVALID_ARG
@@ -306,3 +309,31 @@ def test_query_launch_split(t, d, split, block, grid):
     assert info.workspace_bytes == 16 * t * split
     plain = arf.arfuse_query_launch(8, t, d)
     assert (plain.split, plain.workspace_bytes, plain.grid) == (1, 0, t)
+
+
+# The automatic split for a shape (host-only rule): (n, t, d, layout) -> split
+AUTO = [((8, 8, 8192, 0), 4), ((4, 1, 8192, 0), 4), ((8, 64, 8192, 0), 4), ((8, 128, 8192, 0), 2),
+        ((8, 129, 8192, 0), 1), ((8, 4096, 8192, 0), 1), ((8, 8, 4096, 0), 1), ((2, 1, 4096, 0), 1),
+        ((8, 8, 16384, 0), 8), ((8, 8, 6144, 0), 4), ((8, 8, 8192, 1), 8), ((8, 8, 4096, 1), 4),
+        ((4, 8, 4096, 1), 1), ((8, 8, 2048, 1), 1), ((8, 8, 16384, 1), 8), ((8, 32, 65536, 2), 8),
+        ((8, 33, 65536, 2), 4), ((8, 65, 65536, 0), 1), ((1, 1, 16, 0), 1), ((8, 8, 8208, 0), 1)]
+
+
+@pytest.mark.parametrize("shape,split", AUTO)
+def test_auto_split_choice(shape, split):
+    n, t, d, layout = shape
+    info = arf.arfuse_query_launch(n, t, d, layout=layout, split=arf.ARFUSE_SPLIT_AUTO)
+    assert info.split == split
+    assert info.workspace_bytes == (16 * t * split if split > 1 else 0)
+    assert info.grid == t * split
+    # the choice is what the explicit split would launch
+    if split > 1:
+        ex = arf.arfuse_query_launch(n, t, d, layout=layout, split=split)
+        assert (ex.grid, ex.block, ex.vpt) == (info.grid, info.block, info.vpt)
+
+
+def test_auto_split_needs_the_workspace_it_chose():
+    o = arf._opts(split=arf.ARFUSE_SPLIT_AUTO)
+    assert call(**good(opts=o, d=8192, t=0)) == arf.ARFUSE_OK
+    # t = 8, d = 8192 splits 4 ways: without a workspace the call is refused
+    assert call(**good(opts=o, d=8192)) == arf.ARFUSE_ERR_INVALID_ARG

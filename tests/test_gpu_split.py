@@ -268,3 +268,26 @@ def test_split_out_of_step_workspace_reported():
     c.go(split=split, workspace=ws, status=st)
     check(c.fetch(), ref)
     assert read_status(st) == (0, 0, 0)
+
+
+# ARFUSE_SPLIT_AUTO: the library's choice for the shape, and the workspace
+# that choice needs (one chosen split of each size, and one shape it leaves
+# unsplit, which needs no workspace)
+AUTO = [(8, 8, 8192, 0, dict(fp4=True)), (8, 128, 8192, 0, dict()), (8, 8, 4096, LL, dict()),
+        (8, 8, 16384, SENT, dict(fp8=1.5)), (8, 8, 4096, 0, dict())]
+
+
+@pytest.mark.parametrize("n,t,d,layout,kw", AUTO)
+def test_auto_split_matches_oracle(n, t, d, layout, kw):
+    ci = si.make_call(n, t, d, seed=270 + t + layout, outlier_frac=0.2)
+    ref = reference(ci, **kw)
+    info = arf.arfuse_query_launch(n, t, d, layout=layout, split=arf.ARFUSE_SPLIT_AUTO)
+    c = Call(ci, layout=layout, flag=ci.ll_base + 9, **kw)
+    ws = workspace(t, info.split) if info.split > 1 else None
+    st = new_status()
+    note("auto split n=%d t=%d d=%d layout=%d -> split %d grid %d block %d"
+         % (n, t, d, layout, info.split, info.grid, info.block))
+    for _ in range(2):
+        c.go(split=arf.ARFUSE_SPLIT_AUTO, workspace=ws, status=st, max_polls=1)
+        check(c.fetch(), ref)
+    assert read_status(st) == (0, 0, 0)
