@@ -297,15 +297,19 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
 
 
 def prefill_gbps(n: int, t: int, d: int, steps: int, warmup: int, fp4=False, out=True, seed=0,
-                 **pattern):
-    """Throughput of one fused call shape with rotating buffer sets. `pattern`
-    takes the keyword arguments of `algorithmic_bytes` beyond the shape."""
+                 windows: int = 5, **pattern):
+    """Throughput of one fused call shape with rotating buffer sets: the
+    median of `windows` timed windows of `steps` calls each (a single window
+    can catch a slow spell of the device). `pattern` takes the keyword
+    arguments of `algorithmic_bytes` beyond the shape."""
     import seeded_inputs as si
     ci = si.make_call(n, t, d, seed=seed, outlier_frac=0.001)
     rd, wr = algorithmic_bytes(n, t, d, out=out, fp4=fp4, **pattern)
     sets = PrefillSets(ci, n_sets_for(rd + wr), fp4=fp4, out=out, **pattern)
-    ms = time_calls(sets.call, steps, warmup)
+    per_window = [time_calls(sets.call, steps, warmup if w == 0 else 0) for w in range(windows)]
+    ms = statistics.median(per_window)
     r = dict(n=n, t=t, d=d, fp4=fp4, out=out, nsets=len(sets.sets), us_per_call=ms * 1e3,
+             us_per_call_windows=[round(w * 1e3, 2) for w in per_window],
              read_bytes=rd, write_bytes=wr, algorithmic_gbps=(rd + wr) / (ms * 1e-3) / 1e9,
              **pattern)
     if not fp4 and not pattern:
@@ -553,6 +557,11 @@ def extra_table():
             (8, 8, 8192, 160, "split8", False, "decode_n8_t8_d8192_chain160_split8"),
             (8, 8, 8192, 160, "ll_split4", False, "decode_n8_t8_d8192_chain160_ll_split4"),
             (8, 8, 8192, 160, "sentinel_split4", False, "decode_n8_t8_d8192_chain160_sentinel_split4"),
+            (8, 8, 8192, 160, "ll_split8", False, "decode_n8_t8_d8192_chain160_ll_split8"),
+            (8, 8, 8192, 160, "fresh_split4", False, "decode_n8_t8_d8192_chain160_fresh_split4"),
+            (8, 8, 8192, 160, "sentinel_fresh_split4", False,
+             "decode_n8_t8_d8192_chain160_sentinel_fresh_split4"),
+            (8, 8, 8192, 160, "ll_reused_split8", False, "decode_n8_t8_d8192_chain160_ll_reused_split8"),
             (4, 1, 8192, 100, "split8", True, "fp4_n4_t1_d8192_x100_split8"),
             (4, 8, 8192, 100, "split4", True, "fp4_n4_t8_d8192_x100_split4"),
             # shapes where one workgroup per row leaves most of each CU's time to

@@ -165,11 +165,11 @@ typedef struct {
                                  slice of more than 16,384 elements (or a vpt
                                  override above 2) is ARFUSE_ERR_UNSUPPORTED.
                                  ARFUSE_SPLIT_AUTO: the smallest split whose
-                                 slices take at most 256 threads and 32 KiB
+                                 slices take at most 256 threads and 16 KiB
                                  of partial reads per workgroup, used where
                                  it removes at least two waves per SIMD or
-                                 divides the row at least four ways, else 1;
-                                 a pure function of (n_partials, t, d,
+                                 the whole row reads 128 KiB or more, else
+                                 1; a pure function of (n_partials, t, d,
                                  layout) */
   void* const* reset;         /* SENTINEL: (host) array of n_partials (device)
                                  bf16 [t][d] buffers, 16-byte aligned, that this

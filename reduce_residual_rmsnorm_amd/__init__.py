@@ -160,7 +160,8 @@ def _call_buffers(partials, residual, gamma, out, residual_out, fp4_out, fp4_sca
         fp4_scales=_buf(fp4_scales, t * d // 16, "fp4_scales"),
         fp8_out=_buf(fp8_out, t * d, "fp8_out"),
         status=_buf(status, 16, "status"),
-        workspace=_buf(workspace, 16 * t * max(1, int(split)), "workspace"),
+        # an unsplit call never touches the workspace
+        workspace=_buf(workspace, 16 * t * int(split) if int(split) > 1 else 0, "workspace"),
         reset=None if reset is None else [_buf(r, plane, "reset[%d]" % i)
                                           for i, r in enumerate(reset)])
 
