@@ -353,6 +353,38 @@ def cpu_baseline(ci, budget_s: float = 12.0):
                        "host %s)" % (len(times), ci.n, ci.t, ci.d, med, _cpu_model()))
 
 
+def cpu_baseline_threads(ci, threads: int, budget_s: float = 8.0):
+    """The same oracle on the same calls, its rows cut into `threads` slices
+    that run on parallel host threads (the C oracle runs without Python's
+    lock). The oracle's arithmetic is untouched: this only measures what the
+    host's cores give together."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    orc = oracle.default()
+    bounds = [(ci.t * k // threads, ci.t * (k + 1) // threads) for k in range(threads)]
+
+    def rows(b):
+        a, e = b
+        return orc.allreduce_rmsnorm(ci.partials[:, a:e], ci.residual[a:e], ci.gamma, ci.eps)
+
+    times = []
+    with ThreadPoolExecutor(threads) as ex:
+        t_end = time.time() + budget_s
+        while time.time() < t_end or len(times) < 3:
+            t0 = time.perf_counter()
+            list(ex.map(rows, bounds))
+            times.append(time.perf_counter() - t0)
+            if len(times) >= 50:
+                break
+    med = statistics.median(times)
+    return dict(value=counted_bytes(ci.n, ci.t, ci.d) / med / 1e9, unit="GB/s", cores=threads,
+                kind="oracle",
+                sample="%d full calls of n=%d t=%d d=%d, rows split over %d host threads "
+                       "(median %.3f s/call; host %s)" % (len(times), ci.n, ci.t, ci.d, threads,
+                                                          med, _cpu_model()))
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -655,10 +687,14 @@ def main(argv=None):
     torch.cuda.empty_cache()
 
     extras = {} if args.no_extras else run_extras()
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(ci)
+        # the host's share of cores for one GPU is at most 16 threads
+        threads = max(1, min(16, os.cpu_count() or 1))
+        log("cpu baseline (oracle), rows on %d threads" % threads)
+        cpu_all = cpu_baseline_threads(ci, threads)
 
     traffic = recorded_traffic(name)
     line = {
@@ -686,6 +722,7 @@ def main(argv=None):
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic},
         "cpu_baseline": cpu,
+        "cpu_baseline_threads": cpu_all,
         "kernel_source": source_digest(),
         "extras": extras,
     }
