@@ -131,8 +131,12 @@ def test_ll_wide_row_vpt2():
 class Chain:
     """K chained calls over device buffers; capture into a graph or run eagerly."""
 
-    def __init__(self, n, t, d, k, seed, per_call_sets=False, ll=False):
+    def __init__(self, n, t, d, k, seed, per_call_sets=False, ll=False, split=0):
         self.n, self.t, self.d, self.k = n, t, d, k
+        self.split = split
+        # split rows: one workspace for every call of the chain, zeroed once
+        self.ws = (torch.zeros(16 * t * split, dtype=torch.uint8, device=DEV) if split > 1
+                   else None)
         ci = si.make_call(n, t, d, seed=seed)
         self.ci = ci
         self.flags = [ci.ll_base + c for c in range(k)]
@@ -167,7 +171,10 @@ class Chain:
             if self.ll:
                 arf.arfuse_rmsnorm_ex(self.parts(c), rin, self.gamma, self.ci.eps, self.outs[c], rout,
                                       layout=LL, ll_flag=self.flags[c], max_polls=4,
-                                      status=self.status)
+                                      status=self.status, split=self.split, workspace=self.ws)
+            elif self.split:
+                arf.arfuse_rmsnorm_ex(self.parts(c), rin, self.gamma, self.ci.eps, self.outs[c], rout,
+                                      status=self.status, split=self.split, workspace=self.ws)
             else:
                 arf.arfuse_rmsnorm(self.parts(c), rin, self.gamma, self.ci.eps, self.outs[c], rout)
 
@@ -195,8 +202,9 @@ def check_chain(ch, ref, what):
     outs = host_u16(ch.outs)
     for c in range(ch.k):
         assert_y_close(outs[c], ref[c]["y32"])
-    if ch.ll:
+    if ch.ll or ch.split:
         assert read_status(ch.status) == (0, 0)
+        assert int(ch.status.cpu().numpy().view(np.uint32)[1]) == 0, "exchange timeouts"
 
 
 @pytest.mark.parametrize("n,t,d,k,per_call,ll", [
@@ -229,6 +237,40 @@ def test_graph_chain(n, t, d, k, per_call, ll):
         # eager work between replays
         ch.enqueue()
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n,t,d,k,per_call,ll,split", [
+    (8, 8, 8192, 160, False, False, 4),
+    (8, 8, 8192, 160, True, False, 8),   # fresh partials per call
+    (8, 8, 8192, 160, True, True, 8),    # LL, one partial set and flag per call
+    (4, 8, 4096, 64, False, False, 2),
+])
+def test_graph_chain_split_rows(n, t, d, k, per_call, ll, split):
+    """The same chains with split rows: every call advances the workspace's
+    sequence, in eager runs and graph replays alike."""
+    ch = Chain(n, t, d, k, seed=40 + n, per_call_sets=per_call, ll=ll, split=split)
+    ref = ch.oracle()
+    what = "split chain n=%d d=%d k=%d ll=%s split=%d" % (n, d, k, ll, split)
+    note(what + " eager")
+    ch.enqueue()
+    check_chain(ch, ref, what + " eager")
+    g = torch.cuda.CUDAGraph()
+    note(what + " capture")
+    with torch.cuda.graph(g):
+        ch.enqueue()
+    for rep in range(3):
+        ch.outs.zero_()
+        ch.bufs[0].zero_()
+        ch.bufs[1].zero_()
+        ch.status.zero_()
+        torch.cuda.synchronize()
+        note(what + " replay %d" % rep)
+        g.replay()
+        check_chain(ch, ref, what + " replay %d" % rep)
+        ch.enqueue()
+        torch.cuda.synchronize()
+    seq = ch.ws.cpu().numpy().view(np.uint32).reshape(t * split, 4)[:, 2]
+    assert np.all(seq == 7 * k), "every call advances every slot once"
 
 
 @pytest.mark.parametrize("n,t,d", [(3, 5, 48), (5, 7, 1040), (6, 3, 8208), (2, 2, 65520),

@@ -283,7 +283,8 @@ def test_late_arrival_is_waited_for(layout):
     assert_y_close(host_u16(o), ref["y32"], ref["out"])
 
 
-def test_sentinel_triple_buffered_chain_in_graph():
+@pytest.mark.parametrize("split", [0, 4])
+def test_sentinel_triple_buffered_chain_in_graph(split):
     n, t, d, k = 4, 8, 4096, 12
     ci = si.make_call(n, t, d, seed=82)
     sets = si.make_partial_sets(n, t, d, k, seed=83)
@@ -296,6 +297,7 @@ def test_sentinel_triple_buffered_chain_in_graph():
     outs = torch.empty((k, t, d), dtype=torch.bfloat16, device=DEV)
     st = new_status()
     plane = t * d * 2
+    ws = torch.zeros(16 * t * split, dtype=torch.uint8, device=DEV) if split else None
 
     def enqueue():
         for c in range(k):
@@ -305,10 +307,11 @@ def test_sentinel_triple_buffered_chain_in_graph():
             rin = res0 if c == 0 else bufs[c % 2]
             arf.arfuse_rmsnorm_ex([slots[cur, i] for i in range(n)], rin, g, float(ci.eps),
                                   outs[c], bufs[(c + 1) % 2], layout=SENT, max_polls=4,
-                                  status=st, reset=[slots[nxt, i] for i in range(n)])
+                                  status=st, reset=[slots[nxt, i] for i in range(n)],
+                                  split=split, workspace=ws)
 
     ref = orc().chain(sets, ci.residual, ci.gamma, ci.eps, k)
-    note("sentinel chain eager")
+    note("sentinel chain split=%d eager" % split)
     enqueue()
     torch.cuda.synchronize()
     assert read_status(st) == (0, 0)
@@ -317,7 +320,7 @@ def test_sentinel_triple_buffered_chain_in_graph():
     for s in ((k + 1) % 3, (k + 0) % 3):
         assert np.all(slots[s].cpu().numpy().view(np.uint16) == 0xFFFF), "set %d not reset" % s
     gr = torch.cuda.CUDAGraph()
-    note("sentinel chain capture")
+    note("sentinel chain split=%d capture" % split)
     with torch.cuda.graph(gr):
         enqueue()
     for rep in range(3):
@@ -326,7 +329,7 @@ def test_sentinel_triple_buffered_chain_in_graph():
         bufs[1].zero_()
         st.zero_()
         torch.cuda.synchronize()
-        note("sentinel chain replay %d" % rep)
+        note("sentinel chain split=%d replay %d" % (split, rep))
         gr.replay()
         torch.cuda.synchronize()
         assert read_status(st) == (0, 0)

@@ -291,3 +291,16 @@ def test_auto_split_matches_oracle(n, t, d, layout, kw):
         c.go(split=arf.ARFUSE_SPLIT_AUTO, workspace=ws, status=st, max_polls=1)
         check(c.fetch(), ref)
     assert read_status(st) == (0, 0, 0)
+
+
+def test_split_residual_in_place():
+    """residual_out may be the residual buffer itself: each slice reads its
+    own columns of the residual before it writes them."""
+    n, t, d, split = 8, 8, 8192, 8
+    ci = si.make_call(n, t, d, seed=280, outlier_frac=0.2)
+    ref = reference(ci, fp4=True)
+    c = Call(ci, fp4=True)
+    c.ro = c.res                 # in place
+    note("split in-place residual")
+    c.go(split=split, workspace=workspace(t, split))
+    check(c.fetch(), ref)
