@@ -68,8 +68,11 @@ static void expect(int ok, const char* what) {
 }
 
 /* One fused call on the device against the oracle. epi: ARFUSE_EPI_* mask of
- * the norm outputs besides residual_out (BF16 always, plus FP4 or FP8). */
-static void run_case(int n, int64_t t, int64_t d, int epi, uint64_t seed, hipStream_t stream) {
+ * the norm outputs besides residual_out (BF16 always, plus FP4 or FP8).
+ * split_auto: let the library split the rows (workspace from hipMalloc,
+ * zeroed once), and make the call twice on that workspace. */
+static void run_case(int n, int64_t t, int64_t d, int epi, uint64_t seed, hipStream_t stream,
+                     int split_auto) {
   const int64_t e = t * d;
   const int fp4 = (epi & ARFUSE_EPI_FP4) != 0, fp8 = (epi & ARFUSE_EPI_FP8) != 0;
   const float eps = 1e-5f, inv_scale = 8.0f;
@@ -99,7 +102,28 @@ static void run_case(int n, int64_t t, int64_t d, int epi, uint64_t seed, hipStr
   if (fp8) CHECK_HIP(hipMalloc(&d_fp8, (size_t)e));
 
   int rc;
-  if (fp8) {
+  void* d_ws = NULL;
+  if (split_auto) {
+    arfuse_opts o;
+    memset(&o, 0, sizeof o);
+    o.split = ARFUSE_SPLIT_AUTO;
+    arfuse_launch_info info;
+    expect(arfuse_query_launch(n, t, d, epi, &o, &info) == ARFUSE_OK, "query of the automatic split");
+    printf("[c-demo] automatic split for n=%d t=%lld d=%lld: %d workgroups per row, workspace %lld bytes\n",
+           n, (long long)t, (long long)d, info.split, (long long)info.workspace_bytes);
+    if (info.workspace_bytes > 0) {
+      CHECK_HIP(hipMalloc(&d_ws, (size_t)info.workspace_bytes));
+      CHECK_HIP(hipMemset(d_ws, 0, (size_t)info.workspace_bytes));
+    }
+    o.workspace = d_ws;
+    o.fp8_out = d_fp8;
+    o.fp8_inv_scale = inv_scale;
+    rc = arfuse_rmsnorm_ex((const void* const*)d_parts, n, d_res, d_gamma, eps, d_out, d_rout, d_codes,
+                           d_scales, t, d, stream, &o);
+    if (rc == ARFUSE_OK)  /* the workspace carries over to the next call */
+      rc = arfuse_rmsnorm_ex((const void* const*)d_parts, n, d_res, d_gamma, eps, d_out, d_rout,
+                             d_codes, d_scales, t, d, stream, &o);
+  } else if (fp8) {
     arfuse_opts o;
     memset(&o, 0, sizeof o);
     o.fp8_out = d_fp8;
@@ -171,6 +195,7 @@ static void run_case(int n, int64_t t, int64_t d, int epi, uint64_t seed, hipStr
     CHECK_HIP(hipFree(d_scales));
   }
   if (fp8) CHECK_HIP(hipFree(d_fp8));
+  if (d_ws) CHECK_HIP(hipFree(d_ws));
   free(h_parts);
   free(h_res);
   free(h_gamma);
@@ -203,8 +228,9 @@ int main(void) {
          "nine partials rejected");
   expect(strlen(arfuse_status_string(ARFUSE_ERR_INVALID_ARG)) > 0, "status string");
 
-  run_case(4, 3, 1040, ARFUSE_EPI_BF16 | ARFUSE_EPI_FP4, 11, stream);
-  run_case(8, 2, 8192, ARFUSE_EPI_BF16 | ARFUSE_EPI_FP8, 29, stream);
+  run_case(4, 3, 1040, ARFUSE_EPI_BF16 | ARFUSE_EPI_FP4, 11, stream, 0);
+  run_case(8, 2, 8192, ARFUSE_EPI_BF16 | ARFUSE_EPI_FP8, 29, stream, 0);
+  run_case(8, 8, 8192, ARFUSE_EPI_BF16 | ARFUSE_EPI_FP4, 37, stream, 1);
 
   CHECK_HIP(hipStreamDestroy(stream));
   if (failures) {
