@@ -255,8 +255,14 @@ int arfuse_rmsnorm(const void* const* partials, int n_partials, const void* resi
  * are added in slice order, so the result is deterministic (it may differ in
  * the last bits from the unsplit call, whose sum runs in another order).
  * residual_out, the FP4 and the FP8 outputs are produced per slice exactly as
- * without the split. A share that does not arrive, or a slot already carrying
- * a later sequence, is counted into opts->status (exchange_timeouts).
+ * without the split. The operation is unchanged (the mean square is over the
+ * whole row, Deep Dive §6.3); only the division of the work differs. A share
+ * that does not arrive, or a slot already carrying a later sequence, is
+ * counted into opts->status (exchange_timeouts). The wait for a share is
+ * bounded (2^18 re-reads, a fraction of a second); a split row's workgroups
+ * only ever wait for each other, so work running beside the call on other
+ * streams can delay them but not stall them. The all-reduce alone (gamma
+ * NULL) has no norm and splits without a workspace.
  */
 int arfuse_rmsnorm_ex(const void* const* partials, int n_partials, const void* residual,
                       const float* gamma, float eps, void* out, void* residual_out,
