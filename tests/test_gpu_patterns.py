@@ -241,7 +241,7 @@ def test_sentinel_allreduce_only_with_reset(t):
 
 @pytest.mark.parametrize("layout", [SENT, LL])
 def test_late_arrival_is_waited_for(layout):
-    """A producer on a second stream spins for about a millisecond, then copies
+    """A producer on a second stream spins for a few milliseconds, then copies
     the partials into the slots, while the fused call, already running on the
     current stream, re-reads them: it must see the data arrive (status clean)
     and produce the oracle's result on it. The LL slots start as words with
@@ -265,13 +265,13 @@ def test_late_arrival_is_waited_for(layout):
     torch.cuda.synchronize()
     note("late arrival layout %d" % layout)
     with torch.cuda.stream(producer):
-        torch.cuda._sleep(2_000_000)
+        torch.cuda._sleep(10_000_000)
         for i in range(n):
             arf.arfuse_stream_copy(slots[i], data[i])
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     arf.arfuse_rmsnorm_ex(slots, res, g, float(ci.eps), o, ro, t=t, d=d, layout=layout,
-                          ll_flag=flag, max_polls=100_000, status=st)
+                          ll_flag=flag, max_polls=1_000_000, status=st)
     e1.record()
     torch.cuda.synchronize()
     waited_ms = e0.elapsed_time(e1)
