@@ -326,6 +326,7 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
   a.d8 = d / 8;
   a.ll_flag = opts ? opts->ll_flag : 0;
   a.eps = eps;
+  a.inv_d = 1.0 / (double)d;
   a.fp8_inv_scale = fp8_out ? opts->fp8_inv_scale : 1.0f;
   a.max_polls = opts ? opts->max_polls : 0;
   a.sentinel2 = spat | (spat << 16);

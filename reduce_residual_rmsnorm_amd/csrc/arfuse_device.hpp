@@ -33,6 +33,7 @@ struct RowArgs {
   arfuse_ll_status* status;
   int64_t d8;        // 16-byte bf16 vectors per row (d / 8)
   uint64_t ll_flag;
+  double inv_d;      // 1 / d (the mean's divisor), rounded once on the host
   float eps;
   float fp8_inv_scale;
   uint32_t max_polls;
@@ -214,6 +215,23 @@ __device__ __forceinline__ void store16_through(char* base, uint32_t bytes, uint
 
 // Split rows: bounded wait for a partner's slot (about a quarter second).
 constexpr uint32_t kExchangePolls = 1u << 18;
+
+// 1 / sqrt(ss / d + eps) in fp64: the hardware reciprocal square root
+// refined by two Newton steps on the residual e = 1 - x r^2 (r += r e / 2),
+// each step squaring the relative error, so the result is within a few
+// fp64 ulps of the correctly rounded value. The library's square root and
+// division take about sixty dependent fp64 instructions, which every wave
+// repeats: at four waves per SIMD that cost 0.3 us per decode call.
+__device__ __forceinline__ double inv_rms(double ss, double inv_d, double eps) {
+  const double x = ss * inv_d + eps;
+  double r = __builtin_amdgcn_rsq(x);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const double e = __builtin_fma(-(x * r), r, 1.0);
+    r = __builtin_fma(0.5 * r, e, r);
+  }
+  return r;
+}
 
 // A word whose flag does not match is re-read, a short sleep apart, at most
 // max_polls times. Returns the last word read; *bad counts a word that never
@@ -717,7 +735,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     __syncthreads();
     tot = xsum;
   }
-  const double inv = 1.0 / sqrt(tot / (double)d + (double)a.eps);
+  const double inv = inv_rms(tot, a.inv_d, (double)a.eps);
 
   // ---- normalize, scale by gamma, store bf16 / FP4 / FP8
   if constexpr (!ALL_AT_ONCE) {
