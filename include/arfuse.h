@@ -167,7 +167,7 @@ typedef struct {
                                  ARFUSE_SPLIT_AUTO: the smallest split whose
                                  slices take at most 256 threads and 16 KiB
                                  of partial reads per workgroup, used where
-                                 it removes at least two waves per SIMD or
+                                 it removes at least three waves per SIMD or
                                  the whole row reads 128 KiB or more, else
                                  1; a pure function of (n_partials, t, d,
                                  layout) */

@@ -185,10 +185,10 @@ int64_t work_per_simd(int64_t vecs) {
 // ARFUSE_SPLIT_AUTO: the smallest split whose slices need at most 256 threads
 // (one wave per SIMD at one vector per thread) and read at most 16 KiB of
 // partials per workgroup, within the split limits; kept only where it removes
-// at least two waves' work per SIMD or the unsplit workgroup would read
-// 128 KiB or more. Measured on MI355X decode chains: an exchange costs about
-// 0.5 us, a wave per SIMD about 0.35 us, and a CU fetching data the caches do
-// not hold reads a few tens of GB/s, so a row's bytes are best spread thin.
+// at least three waves' work per SIMD or the unsplit workgroup would read
+// 128 KiB or more. Measured on MI355X decode chains: the exchange costs about
+// 1 us, and a CU fetching data the caches do not hold reads a few tens of
+// GB/s, so a row's bytes are best spread thin once they are many.
 int auto_split_log2(int n, int64_t t, int64_t d, bool ll) {
   const int64_t d8 = d / 8;
   const int64_t vec_bytes = (ll ? 32 : 16) * (int64_t)n;
@@ -196,7 +196,7 @@ int auto_split_log2(int n, int64_t t, int64_t d, bool ll) {
   while (lg < 3 && ((d8 >> lg) > 256 || (d8 >> lg) * vec_bytes > 16384)) ++lg;
   while (lg > 0 && ((t << lg) > ARFUSE_MAX_SPLIT_BLOCKS || d % (16LL << lg))) --lg;
   if (lg == 0 || (d8 >> lg) > kMaxSplitVpt * kMaxBlock) return 0;
-  if (work_per_simd(d8) - work_per_simd(d8 >> lg) < 2 && d8 * vec_bytes < 131072) return 0;
+  if (work_per_simd(d8) - work_per_simd(d8 >> lg) < 3 && d8 * vec_bytes < 131072) return 0;
   return lg;
 }
 

@@ -314,7 +314,7 @@ def test_query_launch_split(t, d, split, block, grid):
 # The automatic split for a shape (host-only rule): (n, t, d, layout) -> split
 AUTO = [((8, 8, 8192, 0), 8), ((4, 1, 8192, 0), 4), ((8, 64, 8192, 0), 4), ((8, 128, 8192, 0), 2),
         ((8, 129, 8192, 0), 1), ((8, 4096, 8192, 0), 1), ((8, 8, 4096, 0), 1), ((2, 1, 4096, 0), 1),
-        ((8, 8, 16384, 0), 8), ((8, 8, 6144, 0), 8), ((8, 8, 8192, 1), 8), ((8, 8, 4096, 1), 8),
+        ((8, 8, 16384, 0), 8), ((8, 8, 6144, 0), 1), ((8, 8, 8192, 1), 8), ((8, 8, 4096, 1), 8),
         ((4, 8, 4096, 1), 1), ((8, 8, 2048, 1), 1), ((8, 8, 16384, 1), 8), ((8, 32, 65536, 2), 8),
         ((8, 33, 65536, 2), 4), ((8, 65, 65536, 0), 1), ((1, 1, 16, 0), 1), ((8, 8, 8208, 0), 1)]
 
