@@ -147,7 +147,9 @@ typedef struct {
                                  between them, before it counts as bad
                                  (0: check once); at most ARFUSE_MAX_POLLS */
   uint64_t ll_flag;           /* LL: the flag every word must carry */
-  arfuse_ll_status* status;   /* LL: (device) status word, or NULL */
+  arfuse_ll_status* status;   /* (device) status word of the LL and sentinel
+                                 layouts and of split rows, 8-byte aligned,
+                                 overlapping no other buffer; or NULL */
   int32_t block_threads;      /* launch override: threads per row block,
                                  a multiple of 64 in [64, 1024]; 0 = auto */
   int32_t vpt;                /* launch override: 16-byte vectors per thread

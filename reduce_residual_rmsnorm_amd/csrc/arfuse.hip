@@ -278,7 +278,7 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
     in[nin++] = range_of(partials[i], pbytes);
   }
   if (gamma && epi != 0) in[nin++] = range_of(gamma, d * 4);
-  Range outs[6 + ARFUSE_MAX_PARTIALS];
+  Range outs[7 + ARFUSE_MAX_PARTIALS];
   int nout = 0;
   const bool rout_first = residual_out != nullptr;
   if (residual_out) outs[nout++] = range_of(residual_out, plane);
@@ -289,6 +289,11 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
   }
   if (fp8_out) outs[nout++] = range_of(fp8_out, t * d);
   if (workspace) outs[nout++] = range_of(workspace, (t << lg) * 16);
+  arfuse_ll_status* status = opts ? opts->status : nullptr;
+  if (status) {  // written by device atomics: 8-byte aligned, shared with nothing
+    if ((uintptr_t)status & 7u) return ARFUSE_ERR_INVALID_ARG;
+    outs[nout++] = range_of(status, (int64_t)sizeof(arfuse_ll_status));
+  }
   if (reset) {
     for (int i = 0; i < n; ++i) {
       if (!reset[i] || !aligned16(reset[i])) return ARFUSE_ERR_INVALID_ARG;

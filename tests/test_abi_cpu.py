@@ -337,3 +337,16 @@ def test_auto_split_needs_the_workspace_it_chose():
     assert call(**good(opts=o, d=8192, t=0)) == arf.ARFUSE_OK
     # t = 8, d = 8192 splits 4 ways: without a workspace the call is refused
     assert call(**good(opts=o, d=8192)) == arf.ARFUSE_ERR_INVALID_ARG
+
+
+def test_status_word_validated():
+    """The status word takes device atomics: it must be 8-byte aligned and
+    must not share memory with the partials or an output."""
+    o = arf._opts(status=spaced(30) + 4)
+    assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
+    o = arf._opts(status=spaced(0) + 64)          # inside partial 0
+    assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
+    o = arf._opts(status=spaced(10) + 16)         # inside out
+    assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
+    o = arf._opts(status=spaced(30))
+    assert call(**good(opts=o, t=0)) == arf.ARFUSE_OK
