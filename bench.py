@@ -207,7 +207,7 @@ def time_graph(g, reps: int):
 
 def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = False,
                  out: bool = True, reps: int = 200, seed: int = 0, fp8: bool = False,
-                 sentinel: bool = False, fresh=None, split: int = 0):
+                 sentinel: bool = False, fresh=None, split: int = 0, norm: bool = True):
     """µs per call of a k-call chain captured in one graph (call c reads call
     c-1's residual_out), and of the same-length graph of the empty kernel
     with the same launch (the per-node floor). `sentinel` reads the slots in
@@ -216,7 +216,8 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
     only) gives every call its own partial buffers, as a peer's push would,
     instead of re-reading one set that stays in the caches. `split` > 1
     divides every row among that many workgroups (sums of squares exchanged
-    through a zeroed workspace)."""
+    through a zeroed workspace). `norm=False` is the all-reduce alone (no
+    gamma: residual_out is the only output)."""
     import numpy as np
     import torch
 
@@ -236,7 +237,8 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
     parts = [[pdev[c % nsets, i] for i in range(n)] for c in range(k)]
     res0 = dev_bf16(ci.residual)
     bufs = [torch.empty_like(res0), torch.empty_like(res0)]
-    gamma = torch.from_numpy(ci.gamma).to(_dev())
+    gamma = torch.from_numpy(ci.gamma).to(_dev()) if norm else None
+    out = out and norm
     o = torch.empty_like(res0) if out else None
     codes = torch.empty((t, d // 2), dtype=torch.uint8, device=_dev()) if fp4 else None
     scales = torch.empty((t, d // 16), dtype=torch.uint8, device=_dev()) if fp4 else None
@@ -256,9 +258,9 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
                 arf.arfuse_rmsnorm_ex(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales,
                                       layout=arf.ARFUSE_LAYOUT_LL, ll_flag=flags[c], max_polls=4,
                                       status=status, **sx)
-            elif sentinel or fp8 or split > 1:
+            elif sentinel or fp8 or split > 1 or not norm:
                 arf.arfuse_rmsnorm_ex(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales,
-                                      layout=arf.ARFUSE_LAYOUT_SENTINEL if sentinel else 0,
+                                      t=t, d=d, layout=arf.ARFUSE_LAYOUT_SENTINEL if sentinel else 0,
                                       max_polls=4, status=status, reset=slots, fp8_out=f8,
                                       fp8_inv_scale=4.0, **sx)
             else:
@@ -285,7 +287,7 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
         raise RuntimeError("arrival reported bad during the benchmark: %s" % st)
     info = arf.arfuse_query_launch(n, t, d, epi, split=split)
     r = dict(n=n, t=t, d=d, calls=k, layout="ll" if ll else "sentinel" if sentinel else "plain",
-             split=max(1, split),
+             split=max(1, split), norm=norm,
              fp4=fp4, fp8=fp8, reset=sentinel, fresh_partials=bool(fresh),
              grid=int(info.grid), block=int(info.block),
              us_per_call_p50=chain["p50"] / k, chain_us_p50=chain["p50"],
@@ -601,13 +603,18 @@ def extra_table():
             (8, 8, 16384, 100, "", False, "decode_n8_t8_d16384_x100"),
             (8, 8, 16384, 100, "split8", False, "decode_n8_t8_d16384_x100_split8"),
             (8, 128, 8192, 50, "", False, "decode_n8_t128_d8192_x50"),
-            (8, 128, 8192, 50, "split2", False, "decode_n8_t128_d8192_x50_split2")]:
+            (8, 128, 8192, 50, "split2", False, "decode_n8_t128_d8192_x50_split2"),
+            # the all-reduce alone (no norm, so no exchange when split)
+            (8, 8, 8192, 160, "allreduce", False, "decode_n8_t8_d8192_chain160_allreduce"),
+            (8, 8, 8192, 160, "allreduce_split8", False,
+             "decode_n8_t8_d8192_chain160_allreduce_split8")]:
         sp = int(mode.split("split")[1]) if "split" in mode else 0
         t[label] = (lambda nn=nn, tt=tt, dd=dd, kk=kk, mode=mode, fp4=fp4, sp=sp:
                     decode_chain(nn, tt, dd, kk, ll=mode.startswith("ll"), fp4=fp4, out=not fp4,
                                  sentinel=mode.startswith("sentinel"), fp8=mode == "fp8",
                                  fresh=(True if "fresh" in mode else False if "reused" in mode
-                                        else None), split=sp))
+                                        else None), split=sp,
+                                 norm=not mode.startswith("allreduce")))
     return t
 
 

@@ -171,8 +171,10 @@ typedef struct {
                                  of partial reads per workgroup, used where
                                  it removes at least three waves per SIMD or
                                  the whole row reads 128 KiB or more, else
-                                 1; a pure function of (n_partials, t, d,
-                                 layout) */
+                                 1; the all-reduce alone (no exchange)
+                                 splits whenever the row reads 32 KiB or
+                                 more. A pure function of (n_partials, t, d,
+                                 layout, whether the call normalizes) */
   void* const* reset;         /* SENTINEL: (host) array of n_partials (device)
                                  bf16 [t][d] buffers, 16-byte aligned, that this
                                  call fills with the sentinel (the slot set a

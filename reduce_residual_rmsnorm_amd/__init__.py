@@ -236,7 +236,10 @@ def arfuse_rmsnorm_ex(partials: Sequence, residual, gamma, eps: float, out, resi
     if ws_split == ARFUSE_SPLIT_AUTO:   # the workspace the library's choice needs
         info = arfuse_launch_info()
         q = _opts(layout=layout, split=split)
-        ws_split = (info.split if lib.arfuse_query_launch(len(partials), t, d, ARFUSE_EPI_BF16,
+        epi = ((ARFUSE_EPI_BF16 if out is not None else 0) |
+               (ARFUSE_EPI_FP4 if fp4_out is not None else 0) |
+               (ARFUSE_EPI_FP8 if fp8_out is not None else 0))
+        ws_split = (info.split if lib.arfuse_query_launch(len(partials), t, d, epi,
                                                           ctypes.byref(q), ctypes.byref(info)) == 0
                     else 1)
     b = _call_buffers(partials, residual, gamma, out, residual_out, fp4_out, fp4_scales, t, d,

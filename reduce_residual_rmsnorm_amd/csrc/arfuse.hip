@@ -189,13 +189,16 @@ int64_t work_per_simd(int64_t vecs) {
 // 128 KiB or more. Measured on MI355X decode chains: the exchange costs about
 // 1 us, and a CU fetching data the caches do not hold reads a few tens of
 // GB/s, so a row's bytes are best spread thin once they are many.
-int auto_split_log2(int n, int64_t t, int64_t d, bool ll) {
+// The all-reduce alone (no norm) needs no exchange, so it splits whenever
+// the row reads 32 KiB or more.
+int auto_split_log2(int n, int64_t t, int64_t d, bool ll, bool norm) {
   const int64_t d8 = d / 8;
   const int64_t vec_bytes = (ll ? 32 : 16) * (int64_t)n;
   int lg = 0;
   while (lg < 3 && ((d8 >> lg) > 256 || (d8 >> lg) * vec_bytes > 16384)) ++lg;
   while (lg > 0 && ((t << lg) > ARFUSE_MAX_SPLIT_BLOCKS || d % (16LL << lg))) --lg;
   if (lg == 0 || (d8 >> lg) > kMaxSplitVpt * kMaxBlock) return 0;
+  if (!norm) return d8 * vec_bytes >= 32768 ? lg : 0;
   if (work_per_simd(d8) - work_per_simd(d8 >> lg) < 3 && d8 * vec_bytes < 131072) return 0;
   return lg;
 }
@@ -203,11 +206,11 @@ int auto_split_log2(int n, int64_t t, int64_t d, bool ll) {
 // Split rows: the validated number of workgroups per row, as its log2 (0 when
 // a row is one workgroup). Every workgroup of a split row must be resident at
 // once, hence the cap on t * split.
-int split_log2(const arfuse_opts* o, int n, int64_t t, int64_t d, int* lg) {
+int split_log2(const arfuse_opts* o, int n, int64_t t, int64_t d, int epi, int* lg) {
   const uint32_t s = o ? o->split : 0u;
   *lg = 0;
   if (s == ARFUSE_SPLIT_AUTO) {
-    *lg = auto_split_log2(n, t, d, o->layout == ARFUSE_LAYOUT_LL);
+    *lg = auto_split_log2(n, t, d, o->layout == ARFUSE_LAYOUT_LL, epi != 0);
     return ARFUSE_OK;
   }
   if (s <= 1) return ARFUSE_OK;
@@ -251,7 +254,7 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
   if (rc) return rc;
   if (!(eps >= 0.0f) || !isfinite(eps)) return ARFUSE_ERR_INVALID_ARG;
   int lg = 0;
-  rc = split_log2(opts, n, t, d, &lg);
+  rc = split_log2(opts, n, t, d, epi, &lg);
   if (rc) return rc;
   int block = 0, vpt = 0;
   rc = row_launch(d, lg, opts, &block, &vpt);
@@ -405,7 +408,7 @@ int arfuse_query_launch(int n_partials, int64_t t, int64_t d, int epilogue,
       opts->layout != ARFUSE_LAYOUT_SENTINEL)
     return ARFUSE_ERR_INVALID_ARG;
   int lg = 0;
-  rc = split_log2(opts, n_partials, t, d, &lg);
+  rc = split_log2(opts, n_partials, t, d, epilogue, &lg);
   if (rc) return rc;
   int block = 0, vpt = 0;
   rc = row_launch(d, lg, opts, &block, &vpt);
@@ -425,7 +428,7 @@ int arfuse_launch_floor(int n_partials, int64_t t, int64_t d, int epilogue,
   int rc = check_shape(n_partials, t, d, epilogue);
   if (rc) return rc;
   int lg = 0;
-  rc = split_log2(opts, n_partials, t, d, &lg);
+  rc = split_log2(opts, n_partials, t, d, epilogue, &lg);
   if (rc) return rc;
   int block = 0, vpt = 0;
   rc = row_launch(d, lg, opts, &block, &vpt);

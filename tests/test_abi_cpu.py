@@ -350,3 +350,15 @@ def test_status_word_validated():
     assert call(**good(opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
     o = arf._opts(status=spaced(30))
     assert call(**good(opts=o, t=0)) == arf.ARFUSE_OK
+
+
+# the all-reduce alone has no exchange: it splits whenever the row reads 32 KiB
+AUTO_NO_NORM = [((8, 8, 8192, 0), 8), ((8, 8, 4096, 0), 4), ((4, 8, 8192, 0), 4),
+                ((2, 1, 4096, 0), 1), ((8, 64, 8192, 0), 4), ((8, 8, 4096, 1), 8)]
+
+
+@pytest.mark.parametrize("shape,split", AUTO_NO_NORM)
+def test_auto_split_choice_without_norm(shape, split):
+    n, t, d, layout = shape
+    info = arf.arfuse_query_launch(n, t, d, 0, layout=layout, split=arf.ARFUSE_SPLIT_AUTO)
+    assert info.split == split

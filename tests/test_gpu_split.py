@@ -274,14 +274,16 @@ def test_split_out_of_step_workspace_reported():
 # that choice needs (one chosen split of each size, and one shape it leaves
 # unsplit, which needs no workspace)
 AUTO = [(8, 8, 8192, 0, dict(fp4=True)), (8, 128, 8192, 0, dict()), (8, 8, 4096, LL, dict()),
-        (8, 8, 16384, SENT, dict(fp8=1.5)), (8, 8, 4096, 0, dict())]
+        (8, 8, 16384, SENT, dict(fp8=1.5)), (8, 8, 4096, 0, dict()),
+        (8, 8, 4096, 0, dict(gamma=False, out=False)), (4, 8, 8192, SENT, dict(gamma=False, out=False))]
 
 
 @pytest.mark.parametrize("n,t,d,layout,kw", AUTO)
 def test_auto_split_matches_oracle(n, t, d, layout, kw):
     ci = si.make_call(n, t, d, seed=270 + t + layout, outlier_frac=0.2)
     ref = reference(ci, **kw)
-    info = arf.arfuse_query_launch(n, t, d, layout=layout, split=arf.ARFUSE_SPLIT_AUTO)
+    epi = 0 if not kw.get("gamma", True) else arf.ARFUSE_EPI_BF16
+    info = arf.arfuse_query_launch(n, t, d, epi, layout=layout, split=arf.ARFUSE_SPLIT_AUTO)
     c = Call(ci, layout=layout, flag=ci.ll_base + 9, **kw)
     ws = workspace(t, info.split) if info.split > 1 else None
     st = new_status()
