@@ -615,9 +615,14 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
       }
     }
     if constexpr (NORM) {
+      // h is fp32, so h * h is exact in fp64 and the fused multiply-add
+      // rounds exactly as the separate product and sum would
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (ok[k][e / 4]) ss += (double)h[k][e] * (double)h[k][e];
+        if (ok[k][e / 4]) {
+          const double hd = (double)h[k][e];
+          ss = __builtin_fma(hd, hd, ss);
+        }
     }
   };
   // refill this row of the slot set a later call reuses; done last, when the
