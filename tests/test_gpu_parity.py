@@ -84,13 +84,16 @@ def test_every_rank_count(n):
     check_call(si.make_call(n, 4, 4096, seed=n))
 
 
-def test_residual_in_place():
-    ci = si.make_call(4, 8, 8192, seed=5)
+# every lane reads its residual elements before it stores residual_out over
+# them, at decode and at prefill-like row counts
+@pytest.mark.parametrize("t,d", [(8, 8192), (300, 4096)])
+def test_residual_in_place(t, d):
+    ci = si.make_call(4, t, d, seed=5)
     orc = __import__("oracle").default()
     ref = orc.allreduce_rmsnorm(ci.partials, ci.residual, ci.gamma, ci.eps)
     dv = Dev(ci)
     dv.residual_out = dv.residual  # in place
-    note("in-place residual")
+    note("in-place residual t=%d d=%d" % (t, d))
     got = dv.run().fetch()
     assert_residual_exact(got["residual_out"], ref["residual_out"])
     assert_y_close(got["out"], ref["y32"])
