@@ -716,7 +716,7 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "dtype_detail": "bf16 storage; fp32 rank-ordered sum and residual add; fp64 RMS and scaling",
+        "dtype_detail": "bf16 storage; fp32 rank-ordered sum and residual add; fp64 sum of squares and inverse RMS; fp32 scaling",
         "data": "synthetic (seeded N(0,1)/sqrt(N) partials, N(0,1) residual with 0.1% x100 rows, "
                 "U(0.5,1.5) gamma)",
         "config": {"workload": name, "n_partials": n, "tokens": t, "hidden": d,

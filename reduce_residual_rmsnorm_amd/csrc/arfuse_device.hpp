@@ -764,7 +764,12 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     __syncthreads();
     tot = xsum;
   }
-  const double inv = inv_rms(tot, a.inv_d, (double)a.eps);
+  // The row's scale in fp64, rounded once to fp32; each element is then
+  // scaled with two fp32 multiplies, y = (h * inv) * gamma. In fp64 the
+  // scaling took five instructions per element (two widenings, two
+  // multiplies, a narrowing) in the part of the call that runs after the
+  // row's loads have landed: 0.1-0.16 us of every decode call.
+  const float inv = (float)inv_rms(tot, a.inv_d, (double)a.eps);
 
   // ---- normalize, scale by gamma, store bf16 / FP4 / FP8
   if constexpr (!ALL_AT_ONCE) {
@@ -787,7 +792,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     const float gg[8] = {g[k][0].x, g[k][0].y, g[k][0].z, g[k][0].w,
                          g[k][1].x, g[k][1].y, g[k][1].z, g[k][1].w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = (float)(((double)h[k][e] * inv) * (double)gg[e]);
+    for (int e = 0; e < 8; ++e) y[e] = (h[k][e] * inv) * gg[e];
     store_residual(k);
     if constexpr (OUT) {
       const u32x4 yb = narrow8(y);
