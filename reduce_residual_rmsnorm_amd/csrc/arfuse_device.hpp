@@ -418,11 +418,17 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   constexpr int D = pipeline_depth<N, VPT, LL>();
   constexpr bool ALL_AT_ONCE = D == VPT;
   constexpr int W = LL ? 2 : 1;  // 16-byte loads per partial per chunk
-  // gamma: with the partials' loads when everything fits at once (not in
-  // the sentinel layout, where it follows the arrival check so the re-poll
-  // path's registers stay free); otherwise per chunk in the output loop
-  constexpr bool G_EARLY = NORM && ALL_AT_ONCE && !SENT;
-  constexpr bool G_AFTER_ARRIVAL = NORM && ALL_AT_ONCE && SENT;
+  // gamma, when the whole row's loads fit at once: a split row's slice loads
+  // it with its partials (plain, LL) or right after the arrival check
+  // (sentinel, so the re-poll path's registers stay free). A whole row loads
+  // it after its rank sum: gamma is not needed before the row's norm, and
+  // left out of the first loads it does not share the one CU's fetch with
+  // the partials (decode chains 0.03-0.07 us faster; split rows, whose
+  // slices fetch little, measured 0.05-0.17 us slower that way). Wide rows
+  // load it per chunk in the output loop.
+  constexpr bool G_EARLY = NORM && ALL_AT_ONCE && SPLIT && !SENT;
+  constexpr bool G_AFTER_ARRIVAL = NORM && ALL_AT_ONCE && SPLIT && SENT;
+  constexpr bool G_AFTER_SUM = NORM && ALL_AT_ONCE && !SPLIT;
   const int lane = threadIdx.x;
   const int nthr = blockDim.x;
   if constexpr (SPLIT) {
@@ -681,6 +687,10 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) rank_sum(k);
+    if constexpr (G_AFTER_SUM) {
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) load_gamma(k);
+    }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) after_sum(k);
   } else {
