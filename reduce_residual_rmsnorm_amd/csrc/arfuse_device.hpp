@@ -108,9 +108,25 @@ __device__ __forceinline__ uint32_t e4m3_rne(float x) {
   return x < 0.015625f ? sub : c;
 }
 
+// fl32(x / 6) for the block scale, without the division sequence: x times
+// fl32(1/6), corrected once by a fused multiply-add of the exact remainder
+// x - 6 q0. It equals the IEEE quotient for every finite x >= 6 * 2^-126
+// (an exhaustive CPU test over every binary32 pattern); below that both are
+// under 2^-126, far under half the smallest E4M3 step (2^-10), so the scale
+// code is 0 either way. The division sequence was about ten dependent
+// instructions per lane.
+__device__ __forceinline__ float div6(float x) {
+  constexpr float kSixth = 1.0f / 6.0f;
+  const float q0 = x * kSixth;
+  return __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, x), kSixth, q0);
+}
+
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
-  if (c < 8u) return (float)c * 0.001953125f;  // c * 2^-9, exact
-  return __uint_as_float((c + (120u << 3)) << 20);
+  // both forms, then a select: written as an early return, the compiler
+  // branched on it
+  const float sub = (float)c * 0.001953125f;  // c * 2^-9, exact
+  const float nrm = __uint_as_float((c + (120u << 3)) << 20);
+  return c < 8u ? sub : nrm;
 }
 
 // E2M1 magnitude code (0, .5, 1, 1.5, 2, 3, 4, 6 -> 0..7) of q = |y| / s,
@@ -169,7 +185,7 @@ __device__ __forceinline__ void fp4_pair(const float y[8], uint32_t& codes8, uin
 #pragma unroll
   for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(y[e]));
   am = fmaxf(am, dpp_f32<0xB1>(am));
-  const uint32_t sc = e4m3_rne(am / 6.0f);
+  const uint32_t sc = e4m3_rne(div6(am));
   const E2M1Thresholds th = e2m1_thresholds(e4m3_value(sc));
   uint32_t c = 0;
 #pragma unroll
@@ -357,7 +373,7 @@ __device__ __forceinline__ void fp4_quad(const float* y, uint32_t& codes4, uint3
   float am = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
   am = fmaxf(am, dpp_f32<0xB1>(am));
   am = fmaxf(am, dpp_f32<0x4E>(am));
-  const uint32_t sc = e4m3_rne(am / 6.0f);
+  const uint32_t sc = e4m3_rne(div6(am));
   const E2M1Thresholds th = e2m1_thresholds(e4m3_value(sc));
   uint32_t c = 0;
 #pragma unroll
