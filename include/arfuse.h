@@ -9,6 +9,8 @@
  *   h         = acc + residual                 fp32, residual added last
  *   residual_out = bf16(h)                      round to nearest even
  *   y         = h / sqrt(mean_j(h^2) + eps) * gamma_j
+ *               (mean of squares and inverse root in fp64; the inverse is
+ *               rounded to fp32 and y = (h * inv) * gamma_j in fp32)
  *   out       = bf16(y)                         optional
  *   FP4       = per 16 consecutive elements of y: scale s = E4M3(max|y| / 6),
  *               code = sign | E2M1(|y| / s)     optional
