@@ -31,7 +31,7 @@
 //    reference.
 //  * FP4 quantizes y32: s = E4M3(fl32(blockmax / 6)) (IEEE division), then
 //    |y| / s rounded to the E2M1 grid with ties to the even code, decided by
-//    exact comparisons with s * threshold (see e2m1_rne).
+//    exact comparisons with s * threshold (see e2m1_two).
 
 #include "arfuse_device.hpp"
 

@@ -138,35 +138,68 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
 // finite |y|: the quotient's rounding can only matter within a couple of ulps
 // of s*T, and an exhaustive sweep there (every scale, every threshold) finds
 // no difference.
-struct E2M1Thresholds {
-  float t[7];
+//
+// The comparisons run on 16-bit keys, two elements per instruction. Each s*T
+// has at most 7 significant bits, so its low 16 bits are zero and its high
+// half K is exact. For a = |y| >= 0 with high half A and low half L:
+//   a >= s*T  <=>  A >= K
+//   a >  s*T  <=>  A + (L != 0) > K
+// (A and K are at most 0x7F80, so 16-bit signed differences do not wrap.)
+// s == 0 gives +inf thresholds (K = 0x7F80), which no finite |y| reaches.
+struct E2M1Keys {
+  // K in both 16-bit halves: the strict thresholds (ties round down) as is,
+  // the others minus one (A >= K <=> K - 1 - A < 0)
+  uint32_t k0, k1m1, k2, k3m1, k4, k5m1, k6;
 };
 
-__device__ __forceinline__ E2M1Thresholds e2m1_thresholds(float s) {
-  // s == 0: every magnitude is 0, which +inf thresholds give for finite |y|
-  const float ss = (s != 0.0f) ? s : __builtin_inff();
-  E2M1Thresholds th{{ss * 0.25f, ss * 0.75f, ss * 1.25f, ss * 1.75f, ss * 2.5f, ss * 3.5f,
-                     ss * 5.0f}};
-  // Keep the seven products in registers: otherwise the compiler rewrites
-  // each element's threshold select as a multiply of s by a selected
-  // constant and turns the nested selects into divergent branches.
-#pragma unroll
-  for (int i = 0; i < 7; ++i) asm("" : "+v"(th.t[i]));
-  return th;
+__device__ __forceinline__ uint32_t rep_hi16(float t) {
+  const uint32_t u = __float_as_uint(t);
+  return __builtin_amdgcn_perm(u, u, 0x03020302u);  // bytes 2,3,2,3
 }
 
-// The magnitude is the number of thresholds |y| passes (strictly for the
-// ties that round down, t[0], t[2], t[4], t[6]); the thresholds ascend, so
-// three comparisons find it: t[3] splits {0..3} from {4..7}, then t[1] or
-// t[5], then one of the strict ones. Selects only, no branches.
-__device__ __forceinline__ uint32_t e2m1_rne(float a, const E2M1Thresholds& th) {
-  const bool b2 = a >= th.t[3];
-  const float mid = b2 ? th.t[5] : th.t[1];
-  const bool b1 = a >= mid;
-  const float lo = b1 ? th.t[2] : th.t[0];
-  const float hi = b1 ? th.t[6] : th.t[4];
-  const float tl = b2 ? hi : lo;
-  return (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (a > tl ? 1u : 0u);
+__device__ __forceinline__ E2M1Keys e2m1_keys(float s) {
+  const float ss = (s != 0.0f) ? s : __builtin_inff();
+  const uint32_t one2 = 0x00010001u;  // no borrow between halves: every K >= 1
+  return E2M1Keys{rep_hi16(ss * 0.25f), rep_hi16(ss * 0.75f) - one2, rep_hi16(ss * 1.25f),
+                  rep_hi16(ss * 1.75f) - one2, rep_hi16(ss * 2.5f), rep_hi16(ss * 3.5f) - one2,
+                  rep_hi16(ss * 5.0f)};
+}
+
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// 0xFFFF in each half where x - y < 0 (16-bit signed), else 0: a packed
+// subtract and a packed arithmetic shift. The mask is hidden from the
+// optimizer, which otherwise turns each bfi() of it into a compare and a
+// select per half.
+__device__ __forceinline__ uint32_t lt16(uint32_t x, uint32_t y) {
+  const i16x2 d = __builtin_bit_cast(i16x2, x) - __builtin_bit_cast(i16x2, y);
+  uint32_t m = __builtin_bit_cast(uint32_t, (i16x2)(d >> (short)15));
+  asm("" : "+v"(m));
+  return m;
+}
+
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t x, uint32_t y) {
+  return (m & x) | (~m & y);
+}
+
+// The 4-bit codes of two elements of one block: y0's in bits 0..3, y1's in
+// bits 16..19 (sign in bit 3 of each). Three levels of comparison find the
+// magnitude, the number of thresholds |y| passes: t3 splits {0..3} from
+// {4..7}, then t1 or t5, then one of the strict ones. No branches.
+__device__ __forceinline__ uint32_t e2m1_two(float y0, float y1, const E2M1Keys& k) {
+  const uint32_t u0 = __float_as_uint(y0), u1 = __float_as_uint(y1);
+  const uint32_t hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);  // high halves
+  const uint32_t a = hi & 0x7FFF7FFFu;
+  // A + (L != 0): the high half of u + 0xFFFF (no carry reaches the sign:
+  // the exponent of a finite value is below 0xFF)
+  const uint32_t ac =
+      __builtin_amdgcn_perm(u1 + 0xFFFFu, u0 + 0xFFFFu, 0x07060302u) & 0x7FFF7FFFu;
+  const uint32_t g2 = lt16(k.k3m1, a);                           // a >= t3
+  const uint32_t g1 = lt16(bfi(g2, k.k5m1, k.k1m1), a);          // a >= t5 or t1
+  const uint32_t tl = bfi(g2, bfi(g1, k.k6, k.k4), bfi(g1, k.k2, k.k0));
+  const uint32_t g0 = lt16(tl, ac);                              // a > t6, t4, t2 or t0
+  return (g0 & 0x00010001u) | (g1 & 0x00020002u) | (g2 & 0x00040004u) |
+         ((hi >> 12) & 0x00080008u);
 }
 
 // Value of lane (lane XOR 1) for CTRL = 0xB1 (quad_perm [1,0,3,2]), of lane
@@ -186,13 +219,12 @@ __device__ __forceinline__ void fp4_pair(const float y[8], uint32_t& codes8, uin
   for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(y[e]));
   am = fmaxf(am, dpp_f32<0xB1>(am));
   const uint32_t sc = e4m3_rne(div6(am));
-  const E2M1Thresholds th = e2m1_thresholds(e4m3_value(sc));
-  uint32_t c = 0;
+  const E2M1Keys k = e2m1_keys(e4m3_value(sc));
+  // elements m and m + 4 share a key pair, so the four pairs' codes land in
+  // place with three shifts: nibble e at bits 4e
+  uint32_t c = e2m1_two(y[0], y[4], k);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t mag = e2m1_rne(fabsf(y[e]), th);
-    c |= (((__float_as_uint(y[e]) >> 31) << 3) | mag) << (4 * e);
-  }
+  for (int m = 1; m < 4; ++m) c |= e2m1_two(y[m], y[m + 4], k) << (4 * m);
   codes8 = c;
   scale = sc;
 }
@@ -374,11 +406,10 @@ __device__ __forceinline__ void fp4_quad(const float* y, uint32_t& codes4, uint3
   am = fmaxf(am, dpp_f32<0xB1>(am));
   am = fmaxf(am, dpp_f32<0x4E>(am));
   const uint32_t sc = e4m3_rne(div6(am));
-  const E2M1Thresholds th = e2m1_thresholds(e4m3_value(sc));
-  uint32_t c = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    c |= (((__float_as_uint(y[e]) >> 31) << 3) | e2m1_rne(fabsf(y[e]), th)) << (4 * e);
+  const E2M1Keys k = e2m1_keys(e4m3_value(sc));
+  // pairs (0, 2) and (1, 3): nibbles 0 and 1 in byte 0, 2 and 3 in byte 2
+  const uint32_t t = e2m1_two(y[0], y[2], k) | (e2m1_two(y[1], y[3], k) << 4);
+  const uint32_t c = __builtin_amdgcn_perm(t, t, 0x0C0C0200u);  // bytes 0, 2
   codes4 = c;
   scale = sc;
 }
