@@ -470,7 +470,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   // (sentinel, so the re-poll path's registers stay free). A whole row loads
   // it after its rank sum: gamma is not needed before the row's norm, and
   // left out of the first loads it does not share the one CU's fetch with
-  // the partials (decode chains 0.03-0.07 us faster; split rows, whose
+  // the partials (decode chains 0.03-0.1 us faster; split rows, whose
   // slices fetch little, measured 0.05-0.17 us slower that way). Wide rows
   // load it per chunk in the output loop.
   constexpr bool G_EARLY = NORM && ALL_AT_ONCE && SPLIT && !SENT;
