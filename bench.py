@@ -598,6 +598,8 @@ def extra_table():
             (8, 8, 8192, 160, "ll_reused_split8", False, "decode_n8_t8_d8192_chain160_ll_reused_split8"),
             (4, 1, 8192, 100, "split8", True, "fp4_n4_t1_d8192_x100_split8"),
             (4, 8, 8192, 100, "split4", True, "fp4_n4_t8_d8192_x100_split4"),
+            (4, 64, 8192, 100, "split4", True, "fp4_n4_t64_d8192_x100_split4"),
+            (8, 8, 8192, 160, "fp8_split8", False, "decode_n8_t8_d8192_chain160_fp8_split8"),
             # shapes where one workgroup per row leaves most of each CU's time to
             # a single row: twice the width, and 128 rows (two rows per CU)
             (8, 8, 16384, 100, "", False, "decode_n8_t8_d16384_x100"),
@@ -611,7 +613,7 @@ def extra_table():
         sp = int(mode.split("split")[1]) if "split" in mode else 0
         t[label] = (lambda nn=nn, tt=tt, dd=dd, kk=kk, mode=mode, fp4=fp4, sp=sp:
                     decode_chain(nn, tt, dd, kk, ll=mode.startswith("ll"), fp4=fp4, out=not fp4,
-                                 sentinel=mode.startswith("sentinel"), fp8=mode == "fp8",
+                                 sentinel=mode.startswith("sentinel"), fp8=mode.startswith("fp8"),
                                  fresh=(True if "fresh" in mode else False if "reused" in mode
                                         else None), split=sp,
                                  norm=not mode.startswith("allreduce")))
