@@ -424,6 +424,9 @@ DECODE_PROFILED = ("decode_n8_t8_d8192_chain160", "decode_n8_t8_d8192_chain160_l
 DECODE_SPLIT_PROFILED = ("decode_n8_t8_d8192_chain160_split4", "decode_n8_t8_d8192_chain160_ll_split4",
                          "decode_n8_t8_d8192_chain160_sentinel_split4", "fp4_n4_t1_d8192_x100_split8")
 
+# single-round prefill calls (512 rows: one workgroup per row, two per CU)
+SMALL_PREFILL_PROFILED = ("prefill_n8_t512_d8192", "fp4_n4_t512_d8192")
+
 PROFILE_COMMANDS = {
     "trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
              "-d $OUT/prof_trace -o prefill -- python3 $REPO/bench.py --steps 50 "
@@ -434,6 +437,12 @@ PROFILE_COMMANDS = {
     "pmc_copy": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {C} --kernel-include-regex "
                 "copy_kernel -f csv -d $OUT/pmc_copy_{C} -o pmc -- python3 "
                 "$REPO/bench.py --copy-only",
+    "trace_small": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
+                   "-d $OUT/prof_small -o small -- python3 $REPO/bench.py "
+                   + " ".join("--only-extra " + x for x in SMALL_PREFILL_PROFILED),
+    "pmc_small": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {C} --kernel-include-regex "
+                 "row_kernel -f csv -d $OUT/pmc_small_{C} -o pmc -- python3 $REPO/bench.py "
+                 + " ".join("--only-extra " + x for x in SMALL_PREFILL_PROFILED),
     "trace_decode": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
                     "-d $OUT/prof_decode -o decode -- python3 $REPO/bench.py "
                     + " ".join("--only-extra " + x for x in DECODE_PROFILED),
@@ -512,6 +521,70 @@ def summarize_profiles(outdir: str) -> None:
     for which in ("decode", "decode_split"):
         if os.path.exists(os.path.join(outdir, "prof_" + which, "decode_kernel_stats.csv")):
             summarize_decode_profile(outdir, which)
+    if os.path.exists(os.path.join(outdir, "prof_small", "small_kernel_stats.csv")):
+        summarize_small_prefill_profile(outdir, kf, kw)
+
+
+# the row-kernel instances of SMALL_PREFILL_PROFILED, as the tracer names them
+SMALL_PREFILL_KERNELS = {
+    "prefill_n8_t512_d8192": ("row_kernel<8, 1, false, false, 1, false>", dict(n=8, t=512, d=8192)),
+    "fp4_n4_t512_d8192": ("row_kernel<4, 1, false, false, 2, false>",
+                          dict(n=4, t=512, d=8192, out=False, fp4=True)),
+}
+
+
+def summarize_small_prefill_profile(outdir: str, kf: float, kw: float) -> None:
+    """profiles/row_kernel_prefill_t512_stats.md and _traffic.json: kernel
+    durations and HBM bytes of the single-round prefill calls, the byte
+    counters scaled by the copy calibration factors (kf, kw) of the same
+    profile run."""
+    import csv
+    line = _bench_line(os.path.join(outdir, "prof_small.log")) or {}
+    rows = list(csv.DictReader(open(os.path.join(outdir, "prof_small", "small_kernel_stats.csv"))))
+    md = ["# row_kernel, single-round prefill calls (t = 512): rocprofv3 kernel statistics", "",
+          "Command (`$REPO` is the repository root, `$OUT` the output directory):", "",
+          "    " + PROFILE_COMMANDS["trace_small"], "",
+          "Kernel source sha256[:16]: `%s`" % source_digest(), "",
+          "Each call reads its own rotated buffer set (7 sets of 92 MB for N = 8; the "
+          "FP4 call's sets likewise exceed the Infinity Cache). Under the tracer the "
+          "dispatches run apart, so each kernel below ran alone on the device.", "",
+          "| kernel | calls | average µs | min µs | max µs | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        md.append("| `%s` | %s | %.2f | %.2f | %.2f | %s |" % (
+            r["Name"].replace("(anonymous namespace)::", ""), r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, r["Percentage"]))
+    rec = {"source_sha256_16": source_digest(), "copy_factors": {"fetch": kf, "write": kw},
+           "commands": [PROFILE_COMMANDS["pmc_small"].format(C=c) for c in ("FETCH_SIZE", "WRITE_SIZE")],
+           "workloads": {}}
+    md += ["", "HBM bytes per dispatch (`FETCH_SIZE`, `WRITE_SIZE`, median over the "
+           "dispatches, scaled by the copy calibration of the same profile run):", "",
+           "| workload | kernel µs (trace average) | read bytes | write bytes | "
+           "over algorithmic | algorithmic GB/s at the trace average |", "|---|---|---|---|---|---|"]
+    for label, (kname, shape) in SMALL_PREFILL_KERNELS.items():
+        fetch, nf = _counter(os.path.join(outdir, "pmc_small_FETCH_SIZE", "pmc_counter_collection.csv"), kname)
+        write, nw = _counter(os.path.join(outdir, "pmc_small_WRITE_SIZE", "pmc_counter_collection.csv"), kname)
+        kw_shape = {k: v for k, v in shape.items() if k not in ("n", "t", "d")}
+        rd, wr = algorithmic_bytes(shape["n"], shape["t"], shape["d"], **kw_shape)
+        rb, wb = fetch * 1024 * kf, write * 1024 * kw
+        avg = [float(r["AverageNs"]) / 1e3 for r in rows if kname in r["Name"]]
+        rec["workloads"][label] = {"kernel": kname, "dispatches": [nf, nw], "read_bytes": rb,
+                                   "write_bytes": wb, "algorithmic_read_bytes": rd,
+                                   "algorithmic_write_bytes": wr,
+                                   "traffic_over_algorithmic": (rb + wb) / (rd + wr),
+                                   "trace_average_us": avg[0] if avg else None}
+        md.append("| %s | %s | %.0f | %.0f | %.4f | %s |" % (
+            label, "%.2f" % avg[0] if avg else "?", rb, wb, (rb + wb) / (rd + wr),
+            "%.0f" % ((rd + wr) / (avg[0] * 1e-6) / 1e9) if avg else "?"))
+    ex = line.get("extras", {})
+    if ex:
+        md += ["", "The same run's events (median window of back-to-back calls, tracer attached):", ""]
+        for k, v in ex.items():
+            md.append("- %s: %.2f µs per call" % (k, v["us_per_call"]))
+    with open(os.path.join(PROFILES, "row_kernel_prefill_t512_stats.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    with open(os.path.join(PROFILES, "row_kernel_prefill_t512_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
 
 
 def summarize_decode_profile(outdir: str, which: str = "decode") -> None:
