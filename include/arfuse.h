@@ -208,7 +208,10 @@ typedef struct {
   int32_t vpt;          /* 16-byte vectors per thread per partial */
   int32_t split;        /* workgroups per row (1 unless opts->split > 1,
                            the choice for ARFUSE_SPLIT_AUTO) */
-  int32_t reserved;
+  int32_t stream_stores; /* 1: the outputs are written through to memory
+                           (calls whose rows take several rounds of
+                           workgroups: t * vpt >= 1024, not LL); 0: non-
+                           temporal stores that may stay in the caches */
   int64_t workspace_bytes; /* bytes of opts->workspace a split call needs */
 } arfuse_launch_info;
 

@@ -67,7 +67,7 @@ class arfuse_opts(ctypes.Structure):
 
 class arfuse_launch_info(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_int64), ("block", ctypes.c_int32), ("vpt", ctypes.c_int32),
-                ("split", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("split", ctypes.c_int32), ("stream_stores", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64)]
 
 

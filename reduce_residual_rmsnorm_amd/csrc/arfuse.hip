@@ -85,16 +85,16 @@ __global__ __launch_bounds__(256) void copy_kernel(const u32x4* src, u32x4* dst,
 
 // ------------------------------------------------------------ dispatch
 
-RowFn select_row_kernel(int n, int vpt, int layout, int epi, bool split) {
+RowFn select_row_kernel(int n, int vpt, int layout, int epi, int kind) {
   switch (n) {
-    case 1: return select_row_kernel_n1(vpt, layout, epi, split);
-    case 2: return select_row_kernel_n2(vpt, layout, epi, split);
-    case 3: return select_row_kernel_n3(vpt, layout, epi, split);
-    case 4: return select_row_kernel_n4(vpt, layout, epi, split);
-    case 5: return select_row_kernel_n5(vpt, layout, epi, split);
-    case 6: return select_row_kernel_n6(vpt, layout, epi, split);
-    case 7: return select_row_kernel_n7(vpt, layout, epi, split);
-    case 8: return select_row_kernel_n8(vpt, layout, epi, split);
+    case 1: return select_row_kernel_n1(vpt, layout, epi, kind);
+    case 2: return select_row_kernel_n2(vpt, layout, epi, kind);
+    case 3: return select_row_kernel_n3(vpt, layout, epi, kind);
+    case 4: return select_row_kernel_n4(vpt, layout, epi, kind);
+    case 5: return select_row_kernel_n5(vpt, layout, epi, kind);
+    case 6: return select_row_kernel_n6(vpt, layout, epi, kind);
+    case 7: return select_row_kernel_n7(vpt, layout, epi, kind);
+    case 8: return select_row_kernel_n8(vpt, layout, epi, kind);
   }
   return nullptr;
 }
@@ -152,6 +152,19 @@ int choose_launch(int64_t d8, const arfuse_opts* o, int* block, int* vpt) {
 // the 256 CUs, so the reset stores run on CUs that would otherwise idle);
 // above it every row block refills its own row.
 constexpr int64_t kSpreadResetRows = 128;
+
+// Rows times vectors per thread at and above which a call runs the
+// streaming-store instances (kRowStream; see out_store): several rounds of
+// workgroups, prefill. Measured better at t=4096 (VPT 1) and t=1024 (VPT 4),
+// no better at t=512 (VPT 1, one round), worse at decode. LL rows have no
+// streaming instances (their words are decode-sized by design).
+constexpr int64_t kStreamStoreChunks = 1024;
+
+int row_kind(int64_t t, int lg, int vpt, int layout) {
+  if (lg != 0) return kRowSplit;
+  if (layout != ARFUSE_LAYOUT_LL && t * vpt >= kStreamStoreChunks) return kRowStream;
+  return kRowWhole;
+}
 
 // Extra reset blocks of a call: N planes of t * d / 8 vectors, one vector per
 // thread. 0 when the rows do the reset themselves or there is none.
@@ -348,7 +361,7 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
   a.plane_vecs = (uint32_t)(t * d / 8);  // only read by reset blocks: t <= 128
   a.reset_bpp = (uint32_t)((t * d / 8 + block - 1) / block);
 
-  const void* fn = (const void*)select_row_kernel(n, vpt, layout, epi, lg != 0);
+  const void* fn = (const void*)select_row_kernel(n, vpt, layout, epi, row_kind(t, lg, vpt, layout));
   if (!fn) return ARFUSE_ERR_UNSUPPORTED;
   void* args[] = {&a};
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)((t << lg) + extra)), dim3((unsigned)block), args, 0,
@@ -418,7 +431,7 @@ int arfuse_query_launch(int n_partials, int64_t t, int64_t d, int epilogue,
   info->block = block;
   info->vpt = vpt;
   info->split = 1 << lg;
-  info->reserved = 0;
+  info->stream_stores = row_kind(t, lg, vpt, opts ? opts->layout : ARFUSE_LAYOUT_PLAIN) == kRowStream;
   info->workspace_bytes = lg ? (t << lg) * 16 : 0;
   return ARFUSE_OK;
 }

@@ -442,6 +442,41 @@ __device__ __forceinline__ T* at_w(char* base, uint32_t off) {
   return reinterpret_cast<T*>(base + off);
 }
 
+// A row output store at byte `off` from the row's base `base` (uniform).
+// Non-temporal by default: at decode the next call reads residual_out right
+// away. STREAM instances (chosen by the host when a call's rows take several
+// rounds of workgroups: prefill) store with device scope (sc1) through a
+// buffer descriptor of the row, which writes through to memory instead of
+// leaving the lines to the L2. Prefill N=8 t=4096 d=8192 121.0 -> 117.2 us,
+// the all-reduce alone 114.3 -> 109.1, d=32768 t=1024 131 -> 122 us, on the
+// same box. A single round of workgroups (t=512) gains nothing, and decode
+// loses 0.25-0.45 us per call with these stores (the next call's reads of
+// residual_out miss), so those keep the non-temporal store. The choice is a
+// template parameter: as a run-time branch it cost every decode call 0.05 us.
+constexpr int kStreamPolicy = 0x10;  // sc1
+template <bool STREAM, typename T>
+__device__ __forceinline__ void out_store(char* base, uint32_t off, T v) {
+  if constexpr (STREAM) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, kBufferWord3);
+    if constexpr (sizeof(T) == 16)
+      __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kStreamPolicy);
+    else if constexpr (sizeof(T) == 8)
+      __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kStreamPolicy);
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kStreamPolicy);
+  } else {
+    __builtin_nontemporal_store(v, at_w<T>(base, off));
+  }
+}
+
+// Row-kernel variants beyond layout and epilogue: one workgroup per row with
+// non-temporal output stores (decode), split rows, or one workgroup per row
+// with streaming stores (prefill; see out_store).
+constexpr int kRowWhole = 0;
+constexpr int kRowSplit = 1;
+constexpr int kRowStream = 2;
+
 // Pipeline depth of a row kernel instance: how many chunks' loads may be in
 // flight while a chunk is processed. A chunk is N partial loads (two words
 // each for LL) plus the residual, 4 VGPRs per 16 bytes; h keeps 8 floats per
@@ -456,8 +491,10 @@ constexpr int pipeline_depth() {
   return 1;
 }
 
-template <int N, int VPT, bool LL, bool SENT, int EPI, bool SPLIT>
+template <int N, int VPT, bool LL, bool SENT, int EPI, int KIND>
 __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
+  constexpr bool SPLIT = KIND == kRowSplit;
+  constexpr bool STREAM = KIND == kRowStream;
   constexpr bool NORM = EPI != 0;
   constexpr bool OUT = (EPI & ARFUSE_EPI_BF16) != 0;
   constexpr bool FP4 = (EPI & ARFUSE_EPI_FP4) != 0;
@@ -678,7 +715,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
         if (ok[k][0]) store8(at_w<u32x2>(orow, eo[k][0] * 2), u32x2{hb.x, hb.y});
         if (ok[k][1]) store8(at_w<u32x2>(orow, eo[k][1] * 2), u32x2{hb.z, hb.w});
       } else if (ok[k][0]) {
-        store16(at_w<u32x4>(orow, eo[k][0] * 2), hb);
+        out_store<STREAM>(orow, eo[k][0] * 2, hb);
       }
     }
   };
@@ -857,7 +894,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
         if (ok[k][0]) store8(at_w<u32x2>(yrow, eo[k][0] * 2), u32x2{yb.x, yb.y});
         if (ok[k][1]) store8(at_w<u32x2>(yrow, eo[k][1] * 2), u32x2{yb.z, yb.w});
       } else if (ok[k][0]) {
-        store16(at_w<u32x4>(yrow, eo[k][0] * 2), yb);
+        out_store<STREAM>(yrow, eo[k][0] * 2, yb);
       }
     }
     if constexpr (FP8) {
@@ -866,7 +903,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
         if (ok[k][0]) __builtin_nontemporal_store(q[0], at_w<uint32_t>(frow, eo[k][0]));
         if (ok[k][1]) __builtin_nontemporal_store(q[1], at_w<uint32_t>(frow, eo[k][1]));
       } else if (ok[k][0]) {
-        store8(at_w<u32x2>(frow, eo[k][0]), u32x2{q[0], q[1]});
+        out_store<STREAM>(frow, eo[k][0], u32x2{q[0], q[1]});
       }
     }
     if constexpr (FP4) {
@@ -884,7 +921,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
         uint32_t c8, sc;
         fp4_pair(y, c8, sc);
         if (ok[k][0]) {
-          __builtin_nontemporal_store(c8, at_w<uint32_t>(crow, eo[k][0] / 2));
+          out_store<STREAM>(crow, eo[k][0] / 2, c8);
           if ((eo[k][0] & 15) == 0) *at_w<uint8_t>(srow, eo[k][0] / 16) = (uint8_t)sc;
         }
       }
@@ -897,13 +934,13 @@ typedef void (*RowFn)(RowArgs);
 
 // Instances for one rank count: returns the kernel for (VPT, layout, EPI);
 // layout is ARFUSE_LAYOUT_PLAIN, _LL or _SENTINEL.
-RowFn select_row_kernel_n1(int vpt, int layout, int epi, bool split);
-RowFn select_row_kernel_n2(int vpt, int layout, int epi, bool split);
-RowFn select_row_kernel_n3(int vpt, int layout, int epi, bool split);
-RowFn select_row_kernel_n4(int vpt, int layout, int epi, bool split);
-RowFn select_row_kernel_n5(int vpt, int layout, int epi, bool split);
-RowFn select_row_kernel_n6(int vpt, int layout, int epi, bool split);
-RowFn select_row_kernel_n7(int vpt, int layout, int epi, bool split);
-RowFn select_row_kernel_n8(int vpt, int layout, int epi, bool split);
+RowFn select_row_kernel_n1(int vpt, int layout, int epi, int kind);
+RowFn select_row_kernel_n2(int vpt, int layout, int epi, int kind);
+RowFn select_row_kernel_n3(int vpt, int layout, int epi, int kind);
+RowFn select_row_kernel_n4(int vpt, int layout, int epi, int kind);
+RowFn select_row_kernel_n5(int vpt, int layout, int epi, int kind);
+RowFn select_row_kernel_n6(int vpt, int layout, int epi, int kind);
+RowFn select_row_kernel_n7(int vpt, int layout, int epi, int kind);
+RowFn select_row_kernel_n8(int vpt, int layout, int epi, int kind);
 
 }  // namespace arfuse_detail

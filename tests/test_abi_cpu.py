@@ -362,3 +362,20 @@ def test_auto_split_choice_without_norm(shape, split):
     n, t, d, layout = shape
     info = arf.arfuse_query_launch(n, t, d, 0, layout=layout, split=arf.ARFUSE_SPLIT_AUTO)
     assert info.split == split
+
+
+def test_query_launch_reports_streaming_stores():
+    """Calls whose rows take several rounds of workgroups (t * vpt >= 1024)
+    write their outputs through to memory; decode-sized calls, split rows and
+    LL calls keep non-temporal stores."""
+    q = arf.arfuse_query_launch
+    assert q(8, 4096, 8192).stream_stores == 1
+    assert q(8, 1024, 8192).stream_stores == 1
+    assert q(8, 1023, 8192).stream_stores == 0
+    assert q(8, 512, 8192).stream_stores == 0
+    assert q(2, 256, 32768).stream_stores == 1          # vpt 4
+    assert q(8, 128, 65536).stream_stores == 1          # vpt 8
+    assert q(8, 4096, 8192, layout=arf.ARFUSE_LAYOUT_LL).stream_stores == 0
+    assert q(8, 4096, 8192, layout=arf.ARFUSE_LAYOUT_SENTINEL).stream_stores == 1
+    assert q(8, 8, 8192, split=4).stream_stores == 0
+    assert q(8, 0, 8192).stream_stores == 0

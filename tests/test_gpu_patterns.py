@@ -339,3 +339,60 @@ def test_sentinel_triple_buffered_chain_in_graph(split):
             assert_y_close(oh[c], ref[c]["y32"])
         enqueue()           # eager work between replays
         torch.cuda.synchronize()
+
+
+# Calls whose rows take several rounds of workgroups (t * vpt >= 1024) run
+# the instances that write their outputs through to memory (streaming
+# stores); every output kind goes through them here, in the plain and the
+# sentinel layout, and in a wide row (four vectors per thread).
+STREAM_PATTERNS = {
+    "bf16": dict(),
+    "fp4": dict(out=False, fp4=True),
+    "bf16_fp4": dict(fp4=True),
+    "fp8": dict(out=False, fp8=2.0),
+    "bf16_fp8": dict(fp8=0.5),
+    "allreduce_only": dict(gamma=False, out=False),
+    "no_residual": dict(residual=False),
+}
+
+
+@pytest.mark.parametrize("layout", [0, SENT])
+@pytest.mark.parametrize("pattern", sorted(STREAM_PATTERNS))
+def test_streaming_store_instances(pattern, layout):
+    kw = STREAM_PATTERNS[pattern]
+    n, t, d = 3, 1024, 1024
+    epi = ((arf.ARFUSE_EPI_BF16 if kw.get("out", True) and kw.get("gamma", True) else 0)
+           | (arf.ARFUSE_EPI_FP4 if kw.get("fp4") else 0)
+           | (arf.ARFUSE_EPI_FP8 if kw.get("fp8") is not None else 0))
+    assert arf.arfuse_query_launch(n, t, d, epi, layout=layout).stream_stores == 1
+    assert arf.arfuse_query_launch(n, 512, d, epi, layout=layout).stream_stores == 0
+    ci = si.make_call(n, t, d, seed=110 + len(pattern), outlier_frac=0.01)
+    ref = orc().fused(ci.partials, ci.residual if kw.get("residual", True) else None,
+                      ci.gamma if kw.get("gamma", True) else None, ci.eps,
+                      out=kw.get("out", True), fp4=kw.get("fp4", False),
+                      fp8_inv_scale=kw.get("fp8"))
+    note("streaming stores %s layout %d t=%d d=%d" % (pattern, layout, t, d))
+    extra = dict(status=new_status(), max_polls=1) if layout == SENT else {}
+    got = run(ci, layout=layout, **kw, **extra)
+    if extra:
+        assert read_status(extra["status"]) == (0, 0)
+    assert_residual_exact(got["residual_out"], ref["residual_out"])
+    if got["out"] is not None:
+        assert_y_close(got["out"], ref["y32"], ref["out"])
+    if got["codes"] is not None:
+        assert_fp4_close(got["codes"], got["scales"], ref["codes"], ref["scales"])
+    if got["fp8"] is not None:
+        assert_fp8_close(got["fp8"], ref["fp8"])
+
+
+def test_streaming_store_wide_rows():
+    n, t, d = 2, 256, 32768
+    info = arf.arfuse_query_launch(n, t, d, arf.ARFUSE_EPI_BF16 | arf.ARFUSE_EPI_FP4)
+    assert info.vpt == 4 and info.stream_stores == 1
+    ci = si.make_call(n, t, d, seed=120, outlier_frac=0.01)
+    ref = orc().fused(ci.partials, ci.residual, ci.gamma, ci.eps, fp4=True)
+    note("streaming stores wide rows t=%d d=%d" % (t, d))
+    got = run(ci, fp4=True)
+    assert_residual_exact(got["residual_out"], ref["residual_out"])
+    assert_y_close(got["out"], ref["y32"], ref["out"])
+    assert_fp4_close(got["codes"], got["scales"], ref["codes"], ref["scales"])
