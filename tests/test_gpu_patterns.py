@@ -199,7 +199,10 @@ def test_sentinel_pending_vectors_reported(sentinel, max_polls):
 
 # t <= 128: extra workgroups of the launch write the reset; above, every row
 # workgroup refills its own row at its end.
-@pytest.mark.parametrize("n,t,d", [(3, 5, 1040), (2, 128, 4096), (3, 129, 1040), (8, 300, 8192)])
+# (2, 1024, 1024): a call of several workgroup rounds (the streaming-store
+# instances) whose rows refill their own slots
+@pytest.mark.parametrize("n,t,d", [(3, 5, 1040), (2, 128, 4096), (3, 129, 1040), (8, 300, 8192),
+                                   (2, 1024, 1024)])
 def test_sentinel_reset_refills_slots(n, t, d):
     ci = si.make_call(n, t, d, seed=81)
     info = arf.arfuse_query_launch(n, t, d, layout=SENT, reset=[1 << 32] * n)
