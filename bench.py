@@ -527,8 +527,8 @@ def summarize_profiles(outdir: str) -> None:
 
 # the row-kernel instances of SMALL_PREFILL_PROFILED, as the tracer names them
 SMALL_PREFILL_KERNELS = {
-    "prefill_n8_t512_d8192": ("row_kernel<8, 1, false, false, 1, false>", dict(n=8, t=512, d=8192)),
-    "fp4_n4_t512_d8192": ("row_kernel<4, 1, false, false, 2, false>",
+    "prefill_n8_t512_d8192": ("row_kernel<8, 1, false, false, 1, 0>", dict(n=8, t=512, d=8192)),
+    "fp4_n4_t512_d8192": ("row_kernel<4, 1, false, false, 2, 0>",
                           dict(n=4, t=512, d=8192, out=False, fp4=True)),
 }
 
