@@ -135,7 +135,10 @@ double oracle_e2m1_value(uint8_t mag_code) { return kE2M1[mag_code & 7]; }
 
 uint8_t oracle_e2m1_rne(float q) {
   double aq = fabs((double)q);
-  if (isinf(aq)) return 7; /* above every value: saturates to 6 */
+  /* 6 is the largest magnitude: every larger q (inf included) is nearer to
+   * it than to any other. Decided here because for q beyond about 2^55 the
+   * distances below are no longer exact in double (they all round to q). */
+  if (aq > 6.0) return 7;
   uint8_t best = 0;
   double bestd = INFINITY;
   for (int c = 0; c < 8; ++c) {
