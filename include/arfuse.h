@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define ARFUSE_VERSION 2
+#define ARFUSE_VERSION 3
 
 /* Largest supported rank count and row width. */
 #define ARFUSE_MAX_PARTIALS 8
@@ -326,6 +326,16 @@ int arfuse_round_bf16(const float* x, int64_t n, uint16_t* out, void* stream);
  * to out (device uint8 [n], 4-byte aligned). n a multiple of 4; x finite.
  */
 int arfuse_round_fp8(const float* x, int64_t n, uint8_t* out, void* stream);
+
+/*
+ * arfuse_round_fp4 — test entry: the conversion the fused kernel's FP4
+ * epilogue takes its E2M1 codes from where both ends of its reciprocal
+ * envelope agree (gfx950's FP4 conversion with scale 1: nearest even,
+ * saturating at 6, sign kept), applied to x (device fp32 [n], 8-byte
+ * aligned), written to out (device uint8 [n/2]: x[2i] in the low nibble of
+ * byte i, x[2i+1] in the high one). n even.
+ */
+int arfuse_round_fp4(const float* x, int64_t n, uint8_t* out, void* stream);
 
 /* Static description of a status code. */
 const char* arfuse_status_string(int status);

@@ -37,6 +37,7 @@ ARFUSE_SPLIT_AUTO = 0xFFFFFFFF
 # The exported functions, as declared in include/arfuse.h.
 EXPORTED = ("arfuse_rmsnorm", "arfuse_rmsnorm_ex", "arfuse_quantize_fp4", "arfuse_query_launch",
             "arfuse_launch_floor", "arfuse_stream_copy", "arfuse_round_bf16", "arfuse_round_fp8",
+            "arfuse_round_fp4",
             "arfuse_status_string", "arfuse_version")
 
 
@@ -101,6 +102,8 @@ def _load(path: str = LIB_PATH):
     lib.arfuse_round_bf16.restype = I
     lib.arfuse_round_fp8.argtypes = [P, I64, P, P]
     lib.arfuse_round_fp8.restype = I
+    lib.arfuse_round_fp4.argtypes = [P, I64, P, P]
+    lib.arfuse_round_fp4.restype = I
     lib.arfuse_status_string.argtypes = [I]
     lib.arfuse_status_string.restype = ctypes.c_char_p
     lib.arfuse_version.argtypes = []
@@ -302,6 +305,14 @@ def arfuse_round_fp8(x, out, stream=None) -> None:
     n = int(x.numel())
     rc = lib.arfuse_round_fp8(_buf(x, 4 * n, "x"), n, _buf(out, n, "out"), _stream(stream))
     _check(rc, "arfuse_round_fp8")
+
+
+def arfuse_round_fp4(x, out, stream=None) -> None:
+    """Test entry: the FP4 conversion of the kernel's fast FP4 path (scale 1)
+    of x (fp32, n even) into out (n / 2 bytes)."""
+    n = int(x.numel())
+    rc = lib.arfuse_round_fp4(_buf(x, 4 * n, "x"), n, _buf(out, n // 2, "out"), _stream(stream))
+    _check(rc, "arfuse_round_fp4")
 
 
 def arfuse_status_string(code: int) -> str:

@@ -78,6 +78,17 @@ __global__ __launch_bounds__(256) void round_fp8_kernel(const f32x4* x, int64_t 
   }
 }
 
+// gfx950's FP4 conversion (scale 1) of fp32 pairs, as the fused kernel's
+// fast FP4 path uses it: byte i holds x[2i] (low nibble) and x[2i + 1].
+__global__ __launch_bounds__(256) void round_fp4_kernel(const f32x2* x, int64_t npairs,
+                                                        uint8_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < npairs) {
+    const f32x2 v = x[i];
+    out[i] = (uint8_t)cvt_fp4x2<0>(0u, v.x, v.y);
+  }
+}
+
 // Streaming copy, 16 bytes per thread: non-temporal loads and the
 // write-through stores of the prefill instances (1 GiB: 6.52 TB/s with
 // non-temporal stores, 6.64 with these).
@@ -507,6 +518,22 @@ int arfuse_round_fp8(const float* x, int64_t n, uint8_t* out, void* stream) {
   int64_t nq = nquads;
   void* args[] = {&xx, &nq, &oo};
   hipError_t e = hipLaunchKernel((const void*)round_fp8_kernel, dim3((unsigned)grid), dim3(256),
+                                 args, 0, (hipStream_t)stream);
+  return launch_status(e);
+}
+
+int arfuse_round_fp4(const float* x, int64_t n, uint8_t* out, void* stream) {
+  if (n < 0 || n % 2) return ARFUSE_ERR_INVALID_ARG;
+  if (n == 0) return ARFUSE_OK;
+  if (!x || !out || ((uintptr_t)x & 7u)) return ARFUSE_ERR_INVALID_ARG;
+  if (overlap(range_of(x, n * 4), range_of(out, n / 2))) return ARFUSE_ERR_INVALID_ARG;
+  const int64_t npairs = n / 2;
+  const int64_t grid = (npairs + 255) / 256;
+  if (grid > 0x7FFFFFFFLL) return ARFUSE_ERR_UNSUPPORTED;
+  const f32x2* xx = (const f32x2*)x;
+  int64_t np = npairs;
+  void* args[] = {&xx, &np, &out};
+  hipError_t e = hipLaunchKernel((const void*)round_fp4_kernel, dim3((unsigned)grid), dim3(256),
                                  args, 0, (hipStream_t)stream);
   return launch_status(e);
 }

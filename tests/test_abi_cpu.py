@@ -37,7 +37,7 @@ def test_symbol_exported(name):
 
 
 def test_version_and_status_strings():
-    assert arf.arfuse_version() == 2
+    assert arf.arfuse_version() == 3
     for code in range(5):
         assert arf.arfuse_status_string(code)
     assert arf.arfuse_status_string(99) == "unknown status"
@@ -226,6 +226,13 @@ def test_quantize_and_copy_validation():
         assert r(spaced(0), 4 * vec, spaced(0) + 4, 0) == arf.ARFUSE_ERR_INVALID_ARG  # overlap
         assert r(spaced(0), 0, 0, 0) == arf.ARFUSE_OK
     assert arf.lib.arfuse_round_fp8(spaced(0) + 8, 4, spaced(1), 0) == arf.ARFUSE_ERR_INVALID_ARG
+    r4 = arf.lib.arfuse_round_fp4
+    assert r4(spaced(0), 3, spaced(1), 0) == arf.ARFUSE_ERR_INVALID_ARG     # odd
+    assert r4(spaced(0), -2, spaced(1), 0) == arf.ARFUSE_ERR_INVALID_ARG
+    assert r4(0, 2, spaced(1), 0) == arf.ARFUSE_ERR_INVALID_ARG
+    assert r4(spaced(0) + 4, 2, spaced(1), 0) == arf.ARFUSE_ERR_INVALID_ARG  # 8-byte alignment
+    assert r4(spaced(0), 8, spaced(0) + 4, 0) == arf.ARFUSE_ERR_INVALID_ARG  # overlap
+    assert r4(spaced(0), 0, 0, 0) == arf.ARFUSE_OK
 
 
 def test_single_hip_runtime_in_process():

@@ -244,6 +244,39 @@ def test_kernel_fp8_conversion_on_every_tie_pattern():
         x[bad[:4]].view(np.uint32), got[bad[:4]], want[bad[:4]])
 
 
+def test_kernel_fp4_conversion_around_every_decision_point():
+    """gfx950's FP4 conversion, as the fused kernel's fast FP4 path uses it
+    (scale 1), equals the oracle's E2M1 rounding (nearest even, saturating,
+    sign kept) at every value within 4096 ulps of each E2M1 value and
+    decision point, both signs, on specials and on random values. The
+    kernel keeps its codes only where both ends of its reciprocal envelope
+    agree, so it relies on this equality near the decision points."""
+    orc = __import__("oracle").default()
+    pts = np.array([0.0, 0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75, 2.0, 2.5, 3.0, 3.5, 4.0, 5.0, 6.0,
+                    7.0, 8.0], np.float32)
+    u = (pts.view(np.int32)[:, None] + np.arange(-4096, 4097, dtype=np.int32)[None, :]).reshape(-1)
+    u = u[(u >= 0) & (u < 0x7F800000)]
+    a = u.view(np.float32)
+    specials = np.array([1e-30, 1e-40, 6.0001, 6.5, 1e3, 1e30, 3.4e38, 0.0], np.float32)
+    rnd = np.random.default_rng(16).standard_normal(1 << 20).astype(np.float32)
+    rnd *= np.exp2(np.random.default_rng(17).integers(-8, 8, rnd.size)).astype(np.float32)
+    x = np.concatenate([a, -a, specials, -specials, rnd]).astype(np.float32)
+    x = x[: x.size // 2 * 2]
+    want = orc.e2m1_rne(np.abs(x)) | np.where(np.signbit(x), 8, 0).astype(np.uint8)
+    xd = dev_f32(x)
+    out = torch.empty(x.size // 2, dtype=torch.uint8, device="cuda:0")
+    note("fp4 conversion sweep n=%d" % x.size)
+    arf.arfuse_round_fp4(xd, out)
+    torch.cuda.synchronize()
+    b = out.cpu().numpy()
+    got = np.empty(x.size, np.uint8)
+    got[0::2] = b & 0xF
+    got[1::2] = b >> 4
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, "fp4 conversion differs at %s: got %s want %s" % (
+        x[bad[:4]], got[bad[:4]], want[bad[:4]])
+
+
 def test_kernel_bf16_rounding_on_every_tie_pattern():
     """The fused kernel's fp32 -> bf16 conversion (gfx950's packed convert)
     equals the oracle's round-to-nearest-even on every 16-bit prefix combined
