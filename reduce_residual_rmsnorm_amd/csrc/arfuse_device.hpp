@@ -94,18 +94,14 @@ __device__ __forceinline__ u32x4 narrow8(const float f[8]) {
 
 // ------------------------------------------------------------- FP4 helpers
 
-// E4M3 (OCP, bias 7, max 448) code of x >= 0, nearest with ties to even.
-// Below 2^-6 the format is fixed point with step 2^-9: x * 512 is exact and
-// rintf rounds half to even, giving codes 0..8 (8 is 2^-6, the first normal
-// code). Otherwise keep 3 mantissa bits of the fp32 pattern with the same
-// carry trick as bf16 (bit 20 is the lowest kept bit); the fp32 exponent
-// minus 120 is the E4M3 exponent field. Above 448 saturate.
-__device__ __forceinline__ uint32_t e4m3_rne(float x) {
-  const uint32_t sub = (uint32_t)rintf(x * 512.0f);
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFFu + ((u >> 20) & 1u);
-  const uint32_t c = min((u >> 20) - (120u << 3), 0x7Eu);
-  return x < 0.015625f ? sub : c;
+// The FP4 block scale: the E4M3 code of x >= 0 (OCP, bias 7, max 448),
+// nearest with ties to even, and its value. gfx950's FP8 conversions do
+// both: the same OCP E4M3 conversion the FP8 output takes (checked against
+// the oracle on every tie pattern), after a clamp to 448 so that larger
+// values saturate, and the matching decode. A bit recipe took about fifteen
+// instructions for the pair.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(x, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
 
 // fl32(x / 6) for the block scale, without the division sequence: x times
@@ -122,11 +118,7 @@ __device__ __forceinline__ float div6(float x) {
 }
 
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
-  // both forms, then a select: written as an early return, the compiler
-  // branched on it
-  const float sub = (float)c * 0.001953125f;  // c * 2^-9, exact
-  const float nrm = __uint_as_float((c + (120u << 3)) << 20);
-  return c < 8u ? sub : nrm;
+  return __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
 }
 
 // E2M1 magnitude code (0, .5, 1, 1.5, 2, 3, 4, 6 -> 0..7) of q = |y| / s,
@@ -247,7 +239,7 @@ __device__ __forceinline__ void fp4_pair(const float y[8], uint32_t& codes8, uin
 #pragma unroll
   for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(y[e]));
   am = fmaxf(am, dpp_f32<0xB1>(am));
-  const uint32_t sc = e4m3_rne(div6(am));
+  const uint32_t sc = e4m3_code(div6(am));
   const float s = e4m3_value(sc);
   const E2M1Envelope r = e2m1_envelope(s);
   uint32_t lo = 0, hi = 0;
@@ -448,7 +440,7 @@ __device__ __forceinline__ void fp4_quad(const float* y, uint32_t& codes4, uint3
   float am = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
   am = fmaxf(am, dpp_f32<0xB1>(am));
   am = fmaxf(am, dpp_f32<0x4E>(am));
-  const uint32_t sc = e4m3_rne(div6(am));
+  const uint32_t sc = e4m3_code(div6(am));
   const float s = e4m3_value(sc);
   const E2M1Envelope r = e2m1_envelope(s);
   uint32_t lo = 0, hi = 0;
