@@ -4,18 +4,24 @@
 //
 // Design (one launch per call, HBM-bound, no matrix cores: the path is not a
 // contraction):
-//  * One workgroup per token row. Thread `lane` owns the 16-byte vectors
-//    v = k * blockDim + lane (k < VPT) of the row, i.e. 8 consecutive bf16
-//    elements per vector; consecutive lanes touch consecutive 16 bytes, so
-//    every wave load is one fully coalesced 1 KiB transaction per partial.
-//  * Every load of the row (N partials, residual, gamma) is issued before any
-//    arithmetic, so a thread keeps N+2 independent 16-byte loads in flight.
+//  * One workgroup per token row (or per slice of a split row). Thread `lane`
+//    owns the 16-byte vectors v = k * blockDim + lane (k < VPT) of the row,
+//    i.e. 8 consecutive bf16 elements per vector; consecutive lanes touch
+//    consecutive 16 bytes, so every wave load is one fully coalesced 1 KiB
+//    transaction per partial.
+//  * While the row fits the registers at once, every partial and residual
+//    load is issued before any arithmetic (gamma follows the rank sum, out of
+//    the partials' fetch); wider rows run as a pipeline of chunks with loads
+//    one or two chunks ahead.
 //  * h stays in VGPRs between the sum and the normalize: no intermediate HBM
 //    round trip (Deep Dive: AllReduce and AllReduce Fusion in TensorRT-LLM,
-//    §6.1 and §6.4).
-//  * The row's sum of squares is reduced across the wave with XOR shuffles,
-//    then across waves through one LDS slot per wave, summed in wave order by
-//    every thread (a fixed tree: deterministic, no atomics).
+//    §6.1 and §6.4). residual_out is stored next to y, after the row's reads.
+//  * The row's sum of squares is reduced across the wave with DPP moves, then
+//    across waves through one LDS slot per wave, summed by the same 16-lane
+//    tree in every wave (a fixed tree: deterministic, no atomics).
+//  * Calls whose rows take several rounds of workgroups (prefill) run
+//    instances whose output stores write through to memory; decode-sized
+//    calls keep non-temporal stores (see out_store).
 //  * Ragged rows (d/8 not a multiple of the block) clamp the vector index of
 //    idle lanes to the last vector, so all loads stay unconditional and in
 //    bounds; clamped lanes store nothing and add nothing.
@@ -24,14 +30,15 @@
 //  * rank sum and residual add: fp32 IEEE adds in rank order, residual last
 //    (built with -ffp-contract=off); residual_out is bf16 round-to-nearest-
 //    even of that h.
-//  * the norm runs in fp64: sum of h^2, mean, 1/sqrt(mean + eps) and
-//    y = (h * inv) * gamma, rounded once to fp32 (y32). MI355X executes fp64
-//    FMAs at the fp32 (non-packed) rate and this kernel is HBM-bound, so the
-//    extra precision costs no time and keeps y32 within an ulp of an fp64
-//    reference.
-//  * FP4 quantizes y32: s = E4M3(fl32(blockmax / 6)) (IEEE division), then
-//    |y| / s rounded to the E2M1 grid with ties to the even code, decided by
-//    exact comparisons with s * threshold (see e2m1_two).
+//  * the norm: sum of h^2 in fp64 (exact squares by FMA), inverse RMS
+//    1/sqrt(mean + eps) in fp64, rounded once to fp32; y = (h * inv) * gamma
+//    by two fp32 multiplies.
+//  * FP4 quantizes y: s = E4M3(fl32(blockmax / 6)) (the quotient exactly as
+//    IEEE division gives it, then gfx950's E4M3 conversion), then |y| / s
+//    rounded to the E2M1 grid with ties to the even code: gfx950's FP4
+//    conversion inside a reciprocal envelope, with exact comparisons against
+//    s * threshold where the envelope leaves a decision open (see
+//    e2m1_envelope and e2m1_two).
 
 #include "arfuse_device.hpp"
 

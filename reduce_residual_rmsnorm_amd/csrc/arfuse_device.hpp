@@ -121,9 +121,11 @@ __device__ __forceinline__ float e4m3_value(uint32_t c) {
   return __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
 }
 
-// E2M1 magnitude code (0, .5, 1, 1.5, 2, 3, 4, 6 -> 0..7) of q = |y| / s,
-// rounded to nearest with ties to the even code: ties at .25, 1.25, 2.5 and 5
-// round down, those at .75, 1.75 and 3.5 round up, above 6 saturates.
+// The exact E2M1 path, taken where the hardware conversion's envelope leaves
+// a decision open (see e2m1_envelope below): the magnitude code (0, .5, 1,
+// 1.5, 2, 3, 4, 6 -> 0..7) of q = |y| / s, rounded to nearest with ties to
+// the even code: ties at .25, 1.25, 2.5 and 5 round down, those at .75, 1.75
+// and 3.5 round up, above 6 saturates.
 // Instead of forming the quotient, |y| is compared with the products s*T,
 // which are exact in fp32 (s has 4 significant bits, T at most 3). This takes
 // the same decision as rounding the correctly rounded fp32 quotient for every
