@@ -799,7 +799,8 @@ def main(argv=None):
                    "bytes_counted_per_step": counted_bytes(n, t, d),
                    "bytes_algorithmic_per_step": rd + wr,
                    "launch": {"grid": int(info.grid), "block": int(info.block),
-                              "vpt": int(info.vpt)}},
+                              "vpt": int(info.vpt),
+                              "stream_stores": int(info.stream_stores)}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic},
