@@ -41,6 +41,9 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Wall",
     "-Wno-unused-function",
+    # the arrival lambda captures the peer-row pointers by value for the
+    # flag and sentinel instances; the plain instances leave them unused
+    "-Wno-unused-lambda-capture",
 ]
 
 
@@ -59,15 +62,23 @@ def build(verbose: bool = False) -> str:
             cmd = [HIPCC, *FLAGS, *defs, "-I", INCLUDE, "-I", CSRC, "-c", "-o", obj, src]
             if verbose:
                 print(" ".join(cmd), flush=True)
-            procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
-                                           text=True), obj, src))
+            # Each compiler writes its diagnostics to a file of its own: a pipe
+            # that is read only after the earlier units finish fills up and
+            # stalls its compiler, which turns the parallel build serial.
+            log = open(os.path.join(tmpdir, name + ".log"), "w+")
+            procs.append((subprocess.Popen(cmd, stdout=log, stderr=subprocess.STDOUT), log, obj))
         objs = []
         failed = False
-        for p, obj, src in procs:
-            out, _ = p.communicate()
+        for p, log, obj in procs:
+            p.wait()
+            log.seek(0)
+            out = log.read()
+            log.close()
             if p.returncode != 0:
                 sys.stderr.write(out)
                 failed = True
+            elif verbose and out:
+                sys.stdout.write(out)
             objs.append(obj)
         if failed:
             raise RuntimeError("hipcc failed building %s" % CSRC)
