@@ -55,8 +55,10 @@
  *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
  *    work; they never synchronize, so they are legal under stream capture.
  *  - Argument errors are returned before anything is enqueued. A failed
- *    launch returns ARFUSE_ERR_LAUNCH. Data-dependent errors (LL flags) are
- *    written to a device status word instead (arfuse_ll_status).
+ *    launch returns ARFUSE_ERR_LAUNCH. Data-dependent errors (LL flags,
+ *    sentinel slots, a split row's exchange) are written to a device status
+ *    word instead (arfuse_ll_status); a call that can wait for data or for
+ *    another workgroup is rejected without one (see arfuse_rmsnorm_ex).
  *  - t == 0 is a no-op: only the shape, eps and the options are validated and
  *    the buffer pointers may be NULL.
  */
@@ -69,7 +71,7 @@
 extern "C" {
 #endif
 
-#define ARFUSE_VERSION 3
+#define ARFUSE_VERSION 4
 
 /* Largest supported rank count and row width. */
 #define ARFUSE_MAX_PARTIALS 8
@@ -123,9 +125,8 @@ typedef struct {
   uint32_t code;      /* 0, or ARFUSE_ERR_FLAG_TIMEOUT: something a row waits
                          for did not arrive within its bounded wait */
   uint32_t exchange_timeouts; /* split rows: partner slots that did not
-                         carry this call's sequence within the bounded wait,
-                         or carried a later one (the workspace is out of step
-                         with the calls); that row's outputs are unspecified */
+                         carry this call's token within the bounded wait;
+                         that row's outputs are unspecified */
   uint64_t bad_words; /* LL words whose flag never matched, or, in the
                          sentinel layout, 16-byte vectors that still held the
                          sentinel after the last re-read */
@@ -149,9 +150,11 @@ typedef struct {
                                  between them, before it counts as bad
                                  (0: check once); at most ARFUSE_MAX_POLLS */
   uint64_t ll_flag;           /* LL: the flag every word must carry */
-  arfuse_ll_status* status;   /* (device) status word of the LL and sentinel
-                                 layouts and of split rows, 8-byte aligned,
-                                 overlapping no other buffer; or NULL */
+  arfuse_ll_status* status;   /* (device) status word, 8-byte aligned,
+                                 overlapping no other buffer. Required (else
+                                 ARFUSE_ERR_INVALID_ARG) by every call that
+                                 can wait: the LL and sentinel layouts, and
+                                 split rows with a norm. NULL otherwise */
   int32_t block_threads;      /* launch override: threads per row block,
                                  a multiple of 64 in [64, 1024]; 0 = auto */
   int32_t vpt;                /* launch override: 16-byte vectors per thread
@@ -189,14 +192,15 @@ typedef struct {
   float fp8_inv_scale;        /* per-tensor reciprocal FP8 scale, finite */
   uint32_t reserved2;         /* must be 0 */
   void* workspace;            /* split rows: (device) t * split 16-byte slots,
-                                 16-byte aligned, zeroed before the first call
-                                 (arfuse_query_launch gives the size). Each
-                                 slot carries a sequence that every call
-                                 advances, so the workspace stays valid across
-                                 calls and graph replays of the same t and
-                                 split; zero it again when either changes.
-                                 Calls sharing a workspace must not overlap.
-                                 NULL when split <= 1 */
+                                 16-byte aligned (arfuse_query_launch gives
+                                 the size). Each slice tags its slot with a
+                                 token of the kernel dispatch (the dispatch's
+                                 index in its hardware queue and the queue),
+                                 so any earlier contents read as "not yet
+                                 written": the workspace needs no clearing,
+                                 before the first call or when t or the
+                                 split changes. Calls sharing a workspace
+                                 must not overlap. NULL when split <= 1 */
 } arfuse_opts;
 
 /* The launch the library would use for a call. */
@@ -255,19 +259,24 @@ int arfuse_rmsnorm(const void* const* partials, int n_partials, const void* resi
  * if given, names buffers the call fills with the sentinel. Words or vectors
  * that never arrive are counted into opts->status (if given); the rows
  * holding them get unspecified outputs. The kernel never waits without
- * bound. opts->fp8_out requests the FP8 output.
+ * bound, and since a wait that gives up is reported only there, these
+ * layouts (and split rows with a norm, below) need opts->status: without it
+ * the call returns ARFUSE_ERR_INVALID_ARG and enqueues nothing (a bounded
+ * wait that gives up must be observable: "Optimizing Tensor Parallelism
+ * Communication Overhead ...", production pitfalls, the timeout break in the
+ * spin loop). opts->fp8_out requests the FP8 output.
  *
  * opts->split > 1 divides every row's columns between that many workgroups
  * (on different CUs). Each computes its columns' share of the sum of squares,
- * writes it with the next sequence to its slot of opts->workspace and waits
- * (bounded) for the row's other slots to carry the same sequence; the shares
+ * writes it with its dispatch's token to its slot of opts->workspace and
+ * waits (bounded) for the row's other slots to carry the same token; the shares
  * are added in slice order, so the result is deterministic (it may differ in
  * the last bits from the unsplit call, whose sum runs in another order).
  * residual_out, the FP4 and the FP8 outputs are produced per slice exactly as
  * without the split. The operation is unchanged (the mean square is over the
  * whole row, Deep Dive §6.3); only the division of the work differs. A share
- * that does not arrive, or a slot already carrying a later sequence, is
- * counted into opts->status (exchange_timeouts). The wait for a share is
+ * that does not arrive is counted into opts->status (exchange_timeouts),
+ * which such a call therefore needs. The wait for a share is
  * bounded (2^18 re-reads, a fraction of a second); a split row's workgroups
  * only ever wait for each other, so work running beside the call on other
  * streams can delay them but not stall them. The all-reduce alone (gamma
@@ -286,6 +295,18 @@ int arfuse_rmsnorm_ex(const void* const* partials, int n_partials, const void* r
  */
 int arfuse_quantize_fp4(const float* y, int64_t t, int64_t d, uint8_t* codes,
                         uint8_t* scales, void* stream);
+
+/*
+ * arfuse_quantize_fp4_ll — test entry: the FP4 epilogue of LL-layout calls
+ * alone, on fp32 y [t][d] (device, 16-byte aligned). In that layout a lane
+ * holds groups of 4 elements and the 4 lanes of a quad hold one 16-element
+ * block; this runs the same device code with thread i on group i (elements
+ * 4i..4i+3 of the flattened y). codes: (device) uint8 [t][d/2], 2-byte
+ * aligned; scales: (device) uint8 [t][d/16]; not overlapping y or each
+ * other. d % 16 == 0. The format is arfuse_quantize_fp4's (Deep Dive §6.5).
+ */
+int arfuse_quantize_fp4_ll(const float* y, int64_t t, int64_t d, uint8_t* codes,
+                           uint8_t* scales, void* stream);
 
 /*
  * arfuse_query_launch — fill *info with the launch a call with these
@@ -311,6 +332,22 @@ int arfuse_launch_floor(int n_partials, int64_t t, int64_t d, int epilogue,
  * achievable HBM bandwidth and for scaling hardware byte counters.
  */
 int arfuse_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
+
+/*
+ * arfuse_stream_mix — measurement aid: the fused call's byte mix without its
+ * arithmetic, in its launch shape. For every row r < t, reads row r of each
+ * of the n_in input planes (device, [t][d] 16-bit elements, 16-byte aligned)
+ * and writes the XOR of them to row r of each of the n_out output planes
+ * (device, [t][d], 16-byte aligned, overlapping no other plane). One
+ * workgroup per row with the block, vectors per thread, load policy and
+ * output store policy the fused call uses for that t and d; every load of a
+ * row is issued before the first store. The time of a call is the bandwidth
+ * ceiling of the fused call's memory traffic at that shape (Deep Dive §6.1,
+ * §6.4: the fused kernel's cost is its HBM transactions). n_in in [1, 9],
+ * n_out in [1, 3]; d % 16 == 0, d <= ARFUSE_MAX_D.
+ */
+int arfuse_stream_mix(const void* const* in, int n_in, void* const* out, int n_out, int64_t t,
+                      int64_t d, void* stream);
 
 /*
  * arfuse_round_bf16 — test entry: the fused kernel's fp32 -> bf16 rounding

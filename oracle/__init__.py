@@ -230,25 +230,27 @@ class Oracle:
             raise ValueError("oracle_ll_unpack rejected its arguments")
         return out, int(bad)
 
-    def chain(self, partial_sets, residual0, gamma, eps, k: int, fp4: bool = False):
-        """Replay ``k`` chained calls: call c consumes call c-1's residual_out.
+    def chain(self, partial_sets, residual0, gamma, eps, k: int, fp4: bool = False,
+              per_call: bool = False):
+        """Replay ``k`` chained calls: call c consumes call c-1's residual_out
+        (Deep Dive: AllReduce and AllReduce Fusion in TensorRT-LLM, §6.2:
+        each layer's fused call takes the residual the previous one wrote).
 
-        ``partial_sets`` is either one list of N partials (the same buffers
-        every call) or a sequence of k such lists. Returns the list of per-call
-        result dicts."""
+        ``per_call=False``: ``partial_sets`` is one sequence of N partials,
+        read by every call (the same buffers). ``per_call=True``: it is a
+        sequence of exactly k such sequences and call c reads the c-th.
+        Returns the list of per-call result dicts."""
+        if per_call and len(partial_sets) != k:
+            raise ValueError("per_call needs one partial set per call (%d sets, %d calls)"
+                             % (len(partial_sets), k))
         res = _c(residual0, np.uint16)
         results = []
         for c in range(k):
-            parts = partial_sets[c] if _is_per_call(partial_sets, k) else partial_sets
+            parts = partial_sets[c] if per_call else partial_sets
             r = self.allreduce_rmsnorm(parts, res, gamma, eps, fp4=fp4)
             results.append(r)
             res = r["residual_out"]
         return results
-
-
-def _is_per_call(partial_sets, k) -> bool:
-    a = np.asarray(partial_sets[0]) if len(partial_sets) else None
-    return a is not None and a.ndim == 3 and len(partial_sets) == k
 
 
 _default: Optional[Oracle] = None

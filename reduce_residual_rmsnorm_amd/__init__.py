@@ -35,9 +35,9 @@ ARFUSE_MAX_SPLIT_BLOCKS = 256
 ARFUSE_SPLIT_AUTO = 0xFFFFFFFF
 
 # The exported functions, as declared in include/arfuse.h.
-EXPORTED = ("arfuse_rmsnorm", "arfuse_rmsnorm_ex", "arfuse_quantize_fp4", "arfuse_query_launch",
-            "arfuse_launch_floor", "arfuse_stream_copy", "arfuse_round_bf16", "arfuse_round_fp8",
-            "arfuse_round_fp4",
+EXPORTED = ("arfuse_rmsnorm", "arfuse_rmsnorm_ex", "arfuse_quantize_fp4", "arfuse_quantize_fp4_ll",
+            "arfuse_query_launch", "arfuse_launch_floor", "arfuse_stream_copy", "arfuse_stream_mix",
+            "arfuse_round_bf16", "arfuse_round_fp8", "arfuse_round_fp4",
             "arfuse_status_string", "arfuse_version")
 
 
@@ -91,6 +91,10 @@ def _load(path: str = LIB_PATH):
     lib.arfuse_rmsnorm_ex.restype = I
     lib.arfuse_quantize_fp4.argtypes = [P, I64, I64, P, P, P]
     lib.arfuse_quantize_fp4.restype = I
+    lib.arfuse_quantize_fp4_ll.argtypes = [P, I64, I64, P, P, P]
+    lib.arfuse_quantize_fp4_ll.restype = I
+    lib.arfuse_stream_mix.argtypes = [P, I, P, I, I64, I64, P]
+    lib.arfuse_stream_mix.restype = I
     lib.arfuse_query_launch.argtypes = [I, I64, I64, I, ctypes.POINTER(arfuse_opts),
                                         ctypes.POINTER(arfuse_launch_info)]
     lib.arfuse_query_launch.restype = I
@@ -264,6 +268,31 @@ def arfuse_quantize_fp4(y, codes, scales, stream=None, t=None, d=None) -> None:
     rc = lib.arfuse_quantize_fp4(_buf(y, 4 * t * d, "y"), t, d, _buf(codes, t * d // 2, "codes"),
                                  _buf(scales, t * d // 16, "scales"), _stream(stream))
     _check(rc, "arfuse_quantize_fp4")
+
+
+def arfuse_quantize_fp4_ll(y, codes, scales, stream=None, t=None, d=None) -> None:
+    """Test entry: the LL-layout FP4 epilogue alone on fp32 y [t][d]; see
+    include/arfuse.h."""
+    if t is None or d is None:
+        t, d = y.shape
+    t, d = int(t), int(d)
+    rc = lib.arfuse_quantize_fp4_ll(_buf(y, 4 * t * d, "y"), t, d,
+                                    _buf(codes, t * d // 2, "codes"),
+                                    _buf(scales, t * d // 16, "scales"), _stream(stream))
+    _check(rc, "arfuse_quantize_fp4_ll")
+
+
+def arfuse_stream_mix(inputs: Sequence, outputs: Sequence, t: int, d: int, stream=None) -> None:
+    """Measurement aid: the fused call's byte mix in its launch shape; see
+    include/arfuse.h."""
+    t, d = int(t), int(d)
+    plane = t * d * 2
+    ia = (ctypes.c_void_p * len(inputs))(*[_buf(x, plane, "inputs[%d]" % i)
+                                           for i, x in enumerate(inputs)])
+    oa = (ctypes.c_void_p * len(outputs))(*[_buf(x, plane, "outputs[%d]" % i)
+                                            for i, x in enumerate(outputs)])
+    rc = lib.arfuse_stream_mix(ia, len(inputs), oa, len(outputs), t, d, _stream(stream))
+    _check(rc, "arfuse_stream_mix")
 
 
 def arfuse_query_launch(n_partials: int, t: int, d: int, epilogue: int = ARFUSE_EPI_BF16,

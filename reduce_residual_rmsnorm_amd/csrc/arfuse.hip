@@ -66,6 +66,76 @@ __global__ __launch_bounds__(256) void quant_kernel(const f32x4* y, int64_t nvec
   }
 }
 
+// FP4 of fp32 y [t][d] in the lane geometry of the LL layout: thread i owns
+// the 4-element group i, so lanes 4m..4m+3 hold one 16-element block, as a
+// wave of an LL row does (fp4_quad, the same 16-bit code store and scale
+// store). d % 16 == 0, so the groups of a block never straddle a row and the
+// 4 lanes of a block are all valid or all idle; idle lanes clamp to the last
+// block.
+__global__ __launch_bounds__(256) void quant_ll_kernel(const f32x4* y, int64_t ngroups,
+                                                       uint16_t* codes, uint8_t* scales) {
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool valid = v < ngroups;
+  const int64_t vc = valid ? v : ngroups - 4 + (v & 3);
+  const f32x4 a = y[vc];
+  const float f[4] = {a.x, a.y, a.z, a.w};
+  uint32_t c4, sc;
+  fp4_quad(f, c4, sc);
+  if (valid) {
+    codes[v] = (uint16_t)c4;
+    if ((v & 3) == 0) scales[v >> 2] = (uint8_t)sc;
+  }
+}
+
+// The fused call's byte mix without its arithmetic: one workgroup per row,
+// the row kernel's lane geometry, vectors per thread, non-temporal loads and
+// output store policy; row r of every output plane receives the XOR of row r
+// of the input planes. Every load of the row is issued before the first use,
+// as in a row-kernel instance that holds its whole row.
+constexpr int kMixMaxIn = ARFUSE_MAX_PARTIALS + 1;
+constexpr int kMixMaxOut = 3;
+struct MixArgs {
+  const u32x4* in[kMixMaxIn];
+  u32x4* out[kMixMaxOut];
+  int64_t d8;
+  int32_t n_in, n_out;
+};
+
+template <int VPT, bool STREAM>
+__global__ __launch_bounds__(kMaxBlock) void mix_kernel(MixArgs a) {
+  const int lane = threadIdx.x;
+  const int nthr = blockDim.x;
+  const uint32_t d8 = (uint32_t)a.d8;
+  const int64_t rb = (int64_t)blockIdx.x * d8 * 16;  // row base, bytes
+  uint32_t off[VPT];
+  bool ok[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const uint32_t v = (uint32_t)(k * nthr + lane);
+    ok[k] = v < d8;
+    off[k] = (ok[k] ? v : d8 - 1) * 16u;
+  }
+  u32x4 raw[VPT][kMixMaxIn];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k)
+#pragma unroll
+    for (int i = 0; i < kMixMaxIn; ++i)
+      if (i < a.n_in) raw[k][i] = load16<true>(at<u32x4>((const char*)a.in[i] + rb, off[k]));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    u32x4 x = raw[k][0];
+#pragma unroll
+    for (int i = 1; i < kMixMaxIn; ++i)
+      if (i < a.n_in) x ^= raw[k][i];
+    if (ok[k]) {
+#pragma unroll
+      for (int o = 0; o < kMixMaxOut; ++o)
+        if (o < a.n_out) out_store<STREAM>((char*)a.out[o] + rb, off[k], x);
+    }
+  }
+}
+
 // The bf16 rounding of the fused kernel applied to an fp32 array (test entry).
 __global__ __launch_bounds__(256) void round_bf16_kernel(const f32x2* x, int64_t npairs,
                                                          uint32_t* out) {
@@ -354,6 +424,13 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
     }
   }
 
+  // A call that can wait (the arrival checks of the LL and sentinel layouts,
+  // a split row's exchange of its sum of squares) gives up after a bounded
+  // wait and then leaves rows unspecified; the status word is the only place
+  // that says so, so such a call must have one.
+  const bool waits = ll || sentinel || (lg != 0 && epi != 0);
+  if (waits && !status) return ARFUSE_ERR_INVALID_ARG;
+
   RowArgs a = {};
   for (int i = 0; i < n; ++i) a.part[i] = (const u32x4*)partials[i];
   if (reset)
@@ -431,6 +508,69 @@ int arfuse_quantize_fp4(const float* y, int64_t t, int64_t d, uint8_t* codes, ui
   void* args[] = {&yy, &nv, &cc, &scales};
   hipError_t e = hipLaunchKernel((const void*)quant_kernel, dim3((unsigned)grid), dim3(256), args,
                                  0, (hipStream_t)stream);
+  return launch_status(e);
+}
+
+int arfuse_quantize_fp4_ll(const float* y, int64_t t, int64_t d, uint8_t* codes, uint8_t* scales,
+                           void* stream) {
+  if (t < 0 || d <= 0 || d % 16) return ARFUSE_ERR_INVALID_ARG;
+  if (t == 0) return ARFUSE_OK;
+  if (!y || !codes || !scales) return ARFUSE_ERR_INVALID_ARG;
+  if (!aligned16(y) || ((uintptr_t)codes & 1u)) return ARFUSE_ERR_INVALID_ARG;
+  const Range ry = range_of(y, t * d * 4), rc = range_of(codes, t * d / 2),
+              rs = range_of(scales, t * d / 16);
+  if (overlap(ry, rc) || overlap(ry, rs) || overlap(rc, rs)) return ARFUSE_ERR_INVALID_ARG;
+  const int64_t ngroups = t * (d / 4);
+  const int64_t grid = (ngroups + 255) / 256;
+  if (grid > 0x7FFFFFFFLL) return ARFUSE_ERR_UNSUPPORTED;
+  const f32x4* yy = (const f32x4*)y;
+  uint16_t* cc = (uint16_t*)codes;
+  int64_t ng = ngroups;
+  void* args[] = {&yy, &ng, &cc, &scales};
+  hipError_t e = hipLaunchKernel((const void*)quant_ll_kernel, dim3((unsigned)grid), dim3(256),
+                                 args, 0, (hipStream_t)stream);
+  return launch_status(e);
+}
+
+int arfuse_stream_mix(const void* const* in, int n_in, void* const* out, int n_out, int64_t t,
+                      int64_t d, void* stream) {
+  if (n_in < 1 || n_in > kMixMaxIn || n_out < 1 || n_out > kMixMaxOut) return ARFUSE_ERR_INVALID_ARG;
+  if (t < 0 || d <= 0 || d % 16) return ARFUSE_ERR_INVALID_ARG;
+  if (d > ARFUSE_MAX_D || t > 0x7FFFFFFFLL) return ARFUSE_ERR_UNSUPPORTED;
+  int block = 0, vpt = 0;
+  int rc = choose_launch(d / 8, nullptr, &block, &vpt);
+  if (rc) return rc;
+  if (t == 0) return ARFUSE_OK;
+  if (!in || !out) return ARFUSE_ERR_INVALID_ARG;
+  const int64_t plane = t * d * 2;
+  MixArgs a = {};
+  for (int i = 0; i < n_in; ++i) {
+    if (!in[i] || !aligned16(in[i])) return ARFUSE_ERR_INVALID_ARG;
+    a.in[i] = (const u32x4*)in[i];
+  }
+  for (int o = 0; o < n_out; ++o) {
+    if (!out[o] || !aligned16(out[o])) return ARFUSE_ERR_INVALID_ARG;
+    for (int i = 0; i < n_in; ++i)
+      if (overlap(range_of(out[o], plane), range_of(in[i], plane))) return ARFUSE_ERR_INVALID_ARG;
+    for (int p = 0; p < o; ++p)
+      if (overlap(range_of(out[o], plane), range_of(out[p], plane))) return ARFUSE_ERR_INVALID_ARG;
+    a.out[o] = (u32x4*)out[o];
+  }
+  a.d8 = d / 8;
+  a.n_in = n_in;
+  a.n_out = n_out;
+  const bool stream_stores = row_kind(t, 0, vpt, ARFUSE_LAYOUT_PLAIN) == kRowStream;
+  const void* fn = nullptr;
+  switch (vpt) {
+    case 1: fn = stream_stores ? (const void*)mix_kernel<1, true> : (const void*)mix_kernel<1, false>; break;
+    case 2: fn = stream_stores ? (const void*)mix_kernel<2, true> : (const void*)mix_kernel<2, false>; break;
+    case 4: fn = stream_stores ? (const void*)mix_kernel<4, true> : (const void*)mix_kernel<4, false>; break;
+    case 8: fn = stream_stores ? (const void*)mix_kernel<8, true> : (const void*)mix_kernel<8, false>; break;
+  }
+  if (!fn) return ARFUSE_ERR_UNSUPPORTED;
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)t), dim3((unsigned)block), args, 0,
+                                 (hipStream_t)stream);
   return launch_status(e);
 }
 

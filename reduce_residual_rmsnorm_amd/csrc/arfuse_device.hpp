@@ -46,7 +46,8 @@ struct RowArgs {
   uint32_t reset_bpp;   // reset blocks per plane (plane_vecs / block, rounded up)
   // split rows: workgroup b < rows << split_log2 takes column slice
   // b & (split - 1) of row b >> split_log2; the slice's workgroups exchange
-  // their sums of squares through ws (slot b: {fp64 partial, sequence, 0})
+  // their sums of squares through ws (slot b: {fp64 partial, 64-bit token of
+  // the dispatch})
   uint32_t split_log2;  // 0: one workgroup per row
   uint32_t ds8;         // 16-byte vectors per slice (d8 >> split_log2)
   u32x4* ws;
@@ -300,6 +301,26 @@ __device__ __forceinline__ void store16_through(char* base, uint32_t bytes, uint
 
 // Split rows: bounded wait for a partner's slot (about a quarter second).
 constexpr uint32_t kExchangePolls = 1u << 18;
+
+// The dispatch id of the running kernel (an SGPR pair the command processor
+// fills at wave launch: the index of the dispatch packet in its queue).
+extern "C" __device__ uint64_t arfuse_llvm_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+// The token a split row's slices tag their exchange slots with: one value
+// per kernel dispatch. Every workgroup of a dispatch reads the same dispatch
+// id, and the command processor numbers the packets of a queue in order, so
+// consecutive calls and graph replays on a queue differ; queues keep their
+// own counts, so the queue's address (another SGPR pair) is mixed into the
+// high word. Bit 0 of the high word is set, so a zeroed slot never matches.
+// A slot carrying any other token (an earlier call of any shape, another
+// queue's call, garbage) reads as "not yet written": the slots need no
+// clearing between calls or when the shape changes.
+__device__ __forceinline__ u32x2 dispatch_token() {
+  const uint64_t did = arfuse_llvm_dispatch_id();
+  const uint64_t q = (uint64_t)__builtin_amdgcn_queue_ptr();
+  return u32x2{(uint32_t)did,
+               ((uint32_t)(q >> 12) ^ (uint32_t)(q >> 44) ^ (uint32_t)(did >> 32)) | 1u};
+}
 
 // 1 / sqrt(ss / d + eps) in fp64: the hardware reciprocal square root
 // refined by two Newton steps on the residual e = 1 - x r^2 (r += r e / 2),
@@ -579,11 +600,11 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   if constexpr (SPLIT) {
     // Split rows: every launch argument the row's first loads depend on, in
     // one batch of scalar loads. The arguments are in memory the scalar cache
-    // has not seen; left to itself the compiler issues them in three batches
-    // (the slot read's branch and the residual's branch split them), each a
-    // memory round trip before the first vector load. Measured on 160-call
-    // chains: 0.05-0.15 us per call. Whole rows keep the compiler's order,
-    // which measured faster for them.
+    // has not seen; left to itself the compiler issued them in several
+    // batches (the residual's branch splits them), each a memory round trip
+    // before the first vector load. Measured on 160-call chains: 0.05-0.15 us
+    // per call. Whole rows keep the compiler's order, which measured faster
+    // for them.
     asm volatile("" ::"s"(a.part[0]), "s"(a.part[1]), "s"(a.part[2]), "s"(a.part[3]),
                  "s"(a.part[4]), "s"(a.part[5]), "s"(a.part[6]), "s"(a.part[7]), "s"(a.residual),
                  "s"(a.gamma), "s"(a.out), "s"(a.residual_out), "s"(a.d8), "s"(a.flags),
@@ -613,14 +634,6 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   const int64_t rb = (int64_t)row * d + (int64_t)slice * ds;  // its first element
   const bool has_res = (a.flags & kHasResidual) != 0;
   const bool has_rout = (a.flags & kHasResidualOut) != 0;
-  // split rows: this workgroup's slot sequence from the previous call, read
-  // right after the row's first loads are issued (by every lane: a branch
-  // here would split the launch arguments' loads), so it overlaps them
-  uint32_t own_seq = 0;
-  auto read_own_seq = [&]() {
-    if constexpr (NORM && SPLIT) own_seq = reread16((const char*)a.ws, row_blocks * 16, blockIdx.x * 16).z;
-  };
-
   // row bases: partials (bf16, or LL words of 4 bytes per element), residual,
   // outputs (bf16), FP4 codes (half a byte per element), scales (1/16), FP8
   const char* prow[N];
@@ -822,7 +835,6 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     // barrier keeps arithmetic out of the load block
 #pragma unroll
     for (int k = 0; k < VPT; ++k) load_chunk(k);
-    read_own_seq();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) arrive(k);
@@ -844,7 +856,6 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     // need more registers than a 1024-thread block has)
 #pragma unroll
     for (int k = 0; k < D; ++k) load_chunk(k);
-    read_own_seq();
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       if (k > 0 && k + D - 1 < VPT) load_chunk(k + D - 1);
@@ -875,19 +886,18 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   const int wl = lane & (kWave - 1);
   double tot = lane_f64(row16_sum<!SPLIT>(wl < nw ? red[wl] : 0.0), 0);
   if constexpr (SPLIT) {
-    // Split row: publish this slice's sum of squares with the next sequence,
-    // then lanes 0..split-1 of wave 0 wait (bounded) for every partner slot
-    // to carry it; the partials are added in slice order, so every slice
-    // computes the same total. A later sequence than expected means the
-    // workspace is out of step with the calls.
+    // Split row: publish this slice's sum of squares tagged with this
+    // dispatch's token, then lanes 0..split-1 of wave 0 wait (bounded) for
+    // every partner slot to carry the same token; the partials are added in
+    // slice order, so every slice computes the same total.
     __shared__ double xsum;
     if (lane < kWave) {
-      const uint32_t seq = (uint32_t)__builtin_amdgcn_readfirstlane((int)own_seq) + 1u;
+      const u32x2 tok = dispatch_token();
       char* wsb = (char*)a.ws;
       const uint32_t wsbytes = row_blocks * 16;
       if (lane == 0) {
         const uint64_t tb = (uint64_t)__double_as_longlong(tot);
-        store16_through(wsb, wsbytes, blockIdx.x * 16, u32x4{(uint32_t)tb, (uint32_t)(tb >> 32), seq, 0u});
+        store16_through(wsb, wsbytes, blockIdx.x * 16, u32x4{(uint32_t)tb, (uint32_t)(tb >> 32), tok.x, tok.y});
       }
       double part = tot;
       uint32_t xbad = 0;
@@ -897,12 +907,10 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
         bool got = false;
         for (uint32_t i = 0; i < kExchangePolls; ++i) {
           w = reread16(wsb, wsbytes, off);
-          const int32_t ahead = (int32_t)(w.z - seq);
-          if (ahead == 0) {
+          if ((w.z == tok.x) & (w.w == tok.y)) {
             got = true;
             break;
           }
-          if (ahead > 0) break;
           if (i >= 64) __builtin_amdgcn_s_sleep(1);
         }
         part = got ? __hiloint2double((int)w.y, (int)w.x) : 0.0;

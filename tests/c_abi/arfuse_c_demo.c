@@ -69,8 +69,9 @@ static void expect(int ok, const char* what) {
 
 /* One fused call on the device against the oracle. epi: ARFUSE_EPI_* mask of
  * the norm outputs besides residual_out (BF16 always, plus FP4 or FP8).
- * split_auto: let the library split the rows (workspace from hipMalloc,
- * zeroed once), and make the call twice on that workspace. */
+ * split_auto: let the library split the rows (workspace from hipMalloc and
+ * filled with a garbage byte: it needs no clearing), make the call twice on
+ * that workspace, and check the status word the split call must have. */
 static void run_case(int n, int64_t t, int64_t d, int epi, uint64_t seed, hipStream_t stream,
                      int split_auto) {
   const int64_t e = t * d;
@@ -103,6 +104,7 @@ static void run_case(int n, int64_t t, int64_t d, int epi, uint64_t seed, hipStr
 
   int rc;
   void* d_ws = NULL;
+  arfuse_ll_status* d_status = NULL;
   if (split_auto) {
     arfuse_opts o;
     memset(&o, 0, sizeof o);
@@ -113,9 +115,19 @@ static void run_case(int n, int64_t t, int64_t d, int epi, uint64_t seed, hipStr
            n, (long long)t, (long long)d, info.split, (long long)info.workspace_bytes);
     if (info.workspace_bytes > 0) {
       CHECK_HIP(hipMalloc(&d_ws, (size_t)info.workspace_bytes));
-      CHECK_HIP(hipMemset(d_ws, 0, (size_t)info.workspace_bytes));
+      CHECK_HIP(hipMemset(d_ws, 0xA5, (size_t)info.workspace_bytes));
     }
+    CHECK_HIP(hipMalloc((void**)&d_status, sizeof(arfuse_ll_status)));
+    CHECK_HIP(hipMemset(d_status, 0, sizeof(arfuse_ll_status)));
     o.workspace = d_ws;
+    o.status = d_status;
+    if (info.split > 1) { /* a split call with a norm waits on its partners: no status, no call */
+      o.status = NULL;
+      expect(arfuse_rmsnorm_ex((const void* const*)d_parts, n, d_res, d_gamma, eps, d_out, d_rout,
+                               d_codes, d_scales, t, d, stream, &o) == ARFUSE_ERR_INVALID_ARG,
+             "split call without a status word rejected");
+      o.status = d_status;
+    }
     o.fp8_out = d_fp8;
     o.fp8_inv_scale = inv_scale;
     rc = arfuse_rmsnorm_ex((const void* const*)d_parts, n, d_res, d_gamma, eps, d_out, d_rout, d_codes,
@@ -150,6 +162,12 @@ static void run_case(int n, int64_t t, int64_t d, int epi, uint64_t seed, hipStr
     CHECK_HIP(hipMemcpy(g_scales, d_scales, (size_t)e / 16, hipMemcpyDeviceToHost));
   }
   if (fp8) CHECK_HIP(hipMemcpy(g_fp8, d_fp8, (size_t)e, hipMemcpyDeviceToHost));
+  if (d_status) {
+    arfuse_ll_status h_status;
+    CHECK_HIP(hipMemcpy(&h_status, d_status, sizeof h_status, hipMemcpyDeviceToHost));
+    expect(h_status.code == 0 && h_status.exchange_timeouts == 0 && h_status.bad_words == 0,
+           "status word clean");
+  }
 
   /* the oracle on the same inputs */
   const uint16_t* parts[8];
@@ -196,6 +214,7 @@ static void run_case(int n, int64_t t, int64_t d, int epi, uint64_t seed, hipStr
   }
   if (fp8) CHECK_HIP(hipFree(d_fp8));
   if (d_ws) CHECK_HIP(hipFree(d_ws));
+  if (d_status) CHECK_HIP(hipFree(d_status));
   free(h_parts);
   free(h_res);
   free(h_gamma);

@@ -521,10 +521,62 @@ def pin_sentinel_pending(orc):
             assert orc.sentinel_pending(a, sentinel) == want
 
 
+# ------------------------------------------------------------ chain pins
+
+def _const_rows(values, d):
+    """bf16 [len(values)][d] whose row i is the constant values[i]."""
+    return si.to_bf16_bits(np.repeat(np.array(values, np.float32)[:, None], d, axis=1))
+
+
+def pin_chain(orc):
+    """The chained replay (call c takes call c-1's residual_out as its
+    residual) against closed forms. Every row of every partial is a constant
+    integer, so each call's sums are exact (integers below 256 are exact in
+    bf16 and fp32): after calls 0..c a row's residual is r0 + s_0 + ... + s_c
+    with s_i that call's rank sum, and each call's y on a constant row h is
+    h / sqrt(h^2 + eps) * gamma (0 on a zero row). With one shared set every
+    call adds the same s, including when the rank count equals the number of
+    calls; with one set per call, call c adds its own s_c, all different, so
+    reading another call's set, or not handing the residual on, changes some
+    call's residual_out."""
+    d = 16
+    gamma = np.linspace(0.5, 1.5, d).astype(np.float32)
+    eps = np.float32(1e-5)
+    r0 = [3.0, -2.0]
+
+    def check(results, sums, what):
+        assert len(results) == len(sums), what
+        h = np.array(r0, np.float64)
+        for c, r in enumerate(results):
+            h = h + np.array(sums[c], np.float64)
+            assert np.array_equal(r["residual_out"], _const_rows(h, d)), \
+                "%s: call %d residual_out is not the running sum %s" % (what, c, h)
+            want = (h / np.sqrt(h * h + float(eps)))[:, None] * gamma.astype(np.float64)[None, :]
+            assert np.allclose(r["y32"].astype(np.float64), want, rtol=1e-6, atol=0), \
+                "%s: call %d y" % (what, c)
+
+    # one shared set of 4 ranks, 4 calls (row sums 2 and 1; row 1 passes 0)
+    ranks = [[2.0, -1.0], [-1.0, 3.0], [1.0, 0.0], [0.0, -1.0]]
+    shared = [_const_rows(v, d) for v in ranks]
+    check(orc.chain(shared, _const_rows(r0, d), gamma, eps, 4), [[2.0, 1.0]] * 4, "shared set")
+    # one set of 3 ranks per call, call c sums to (c + 1, -(2c + 1))
+    k = 5
+    sets, sums = [], []
+    for c in range(k):
+        sets.append([_const_rows(v, d) for v in ([c + 1.0, -(2.0 * c + 1)], [1.0, 1.0], [-1.0, -1.0])])
+        sums.append([c + 1.0, -(2.0 * c + 1)])
+    check(orc.chain(sets, _const_rows(r0, d), gamma, eps, k, per_call=True), sums, "per-call sets")
+    # a one-call chain is the fused call itself
+    one = orc.chain(sets[:1], _const_rows(r0, d), gamma, eps, 1, per_call=True)
+    full = orc.allreduce_rmsnorm(sets[0], _const_rows(r0, d), gamma, eps)
+    assert np.array_equal(one[0]["residual_out"], full["residual_out"])
+    assert np.array_equal(one[0]["y32"], full["y32"])
+
+
 ALL_PINS = [
     pin_bf16_vs_torch, pin_e4m3_decode_vs_torch, pin_e4m3_rne_exact, pin_e2m1_rne_exact,
     pin_fp4_code_ties, pin_fp4_scale_ties, pin_fp4_small_random_blocks, pin_fp4_invariants,
     pin_rank_order, pin_summation_bound, pin_residual_out_is_bf16_of_h,
     pin_rmsnorm_vs_torch_f64, pin_fused_uses_fp32_h, pin_closed_forms, pin_scale_invariance,
-    pin_ll_roundtrip, pin_fp8_exact, pin_patterns, pin_sentinel_pending,
+    pin_ll_roundtrip, pin_fp8_exact, pin_patterns, pin_sentinel_pending, pin_chain,
 ]

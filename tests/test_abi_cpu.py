@@ -37,7 +37,7 @@ def test_symbol_exported(name):
 
 
 def test_version_and_status_strings():
-    assert arf.arfuse_version() == 3
+    assert arf.arfuse_version() == 4
     for code in range(5):
         assert arf.arfuse_status_string(code)
     assert arf.arfuse_status_string(99) == "unknown status"
@@ -174,8 +174,24 @@ def test_ll_partials_occupy_twice_the_bytes():
     # plane after a partial: valid for plain, overlapping for LL.
     kw = good(out=spaced(0) + PLANE)
     assert call(**dict(kw, t=0)) == arf.ARFUSE_OK
-    o = arf._opts(layout=arf.ARFUSE_LAYOUT_LL)
+    o = arf._opts(layout=arf.ARFUSE_LAYOUT_LL, status=spaced(30))
     assert call(**dict(kw, opts=o)) == arf.ARFUSE_ERR_INVALID_ARG
+
+
+def test_waiting_calls_need_a_status_word():
+    """A call that can wait (LL or sentinel arrival, a split row's exchange)
+    reports a bounded wait that gave up only in its status word, so without
+    one it is refused before anything is enqueued. (With one, the same calls
+    pass validation: checked in the sanitized host build, which stops at an
+    empty kernel selector instead of launching.)"""
+    INV = arf.ARFUSE_ERR_INVALID_ARG
+    ws = spaced(40)
+    for o in (arf._opts(layout=arf.ARFUSE_LAYOUT_LL), arf._opts(layout=arf.ARFUSE_LAYOUT_SENTINEL),
+              arf._opts(split=4, workspace=ws), arf._opts(split=arf.ARFUSE_SPLIT_AUTO, workspace=ws)):
+        assert call(**good(opts=o, d=8192)) == INV
+        assert call(**good(opts=o, d=8192, t=0)) == arf.ARFUSE_OK   # t = 0 stays a no-op
+    # the automatic choice above does split at this shape
+    assert arf.arfuse_query_launch(4, T, 8192, split=arf.ARFUSE_SPLIT_AUTO).split > 1
 
 
 @pytest.mark.parametrize("d,block,vpt", [(16, 64, 1), (4096, 512, 1), (8192, 1024, 1),

@@ -128,6 +128,8 @@ int main() {
   o.reset = slots;
   EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 4, 4096, nullptr, &o), INV);
   o.layout = ARFUSE_LAYOUT_SENTINEL;
+  EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 4, 4096, nullptr, &o), INV);
+  o.status = (arfuse_ll_status*)A(18);
   EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 4, 4096, nullptr, &o), UNS);
   std::memset(&o, 0, sizeof o);
   o.fp8_out = (uint8_t*)A(16);
@@ -141,14 +143,68 @@ int main() {
   o.workspace = (char*)A(17) + 8;
   EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 4, 4096, nullptr, &o), INV);
   o.workspace = A(17);
+  EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 4, 4096, nullptr, &o), INV);
+  o.status = (arfuse_ll_status*)A(18);
   EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 4, 4096, nullptr, &o), UNS);
+  o.status = nullptr;
   o.split = 8;
   EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 64, 4096, nullptr, &o), UNS);
   EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 33, 4096, nullptr, &o), UNS);
   o.status = (arfuse_ll_status*)((char*)A(18) + 4);
   EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 4, 4096, nullptr, &o), INV);
 
+  // every call that can wait needs a status word (the only report of a
+  // bounded wait that gave up); with one, each passes validation
+  {
+    arfuse_ll_status* st = (arfuse_ll_status*)A(18);
+    const int lay[3] = {ARFUSE_LAYOUT_LL, ARFUSE_LAYOUT_SENTINEL, ARFUSE_LAYOUT_PLAIN};
+    const uint32_t spl[3] = {0u, 0u, 4u};
+    for (int c = 0; c < 3; ++c) {
+      std::memset(&o, 0, sizeof o);
+      o.layout = lay[c];
+      o.split = spl[c];
+      o.workspace = spl[c] ? A(17) : nullptr;
+      EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 4, 8192, nullptr, &o), INV);
+      o.status = st;
+      EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 4, 8192, nullptr, &o), UNS);
+    }
+    // the library's own choice: n = 2, t = 4, d = 8192 splits 4 ways
+    std::memset(&o, 0, sizeof o);
+    o.split = ARFUSE_SPLIT_AUTO;
+    o.workspace = A(17);
+    EXPECT(arfuse_query_launch(2, 4, 8192, 1, &o, &info), OK);
+    EXPECT(info.split, 4);
+    EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 4, 8192, nullptr, &o), INV);
+    o.status = st;
+    EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 4, 8192, nullptr, &o), UNS);
+    // the all-reduce alone never waits: no status needed, split or not
+    std::memset(&o, 0, sizeof o);
+    o.split = 4;
+    EXPECT(arfuse_rmsnorm_ex(parts, 2, res, nullptr, 1e-5f, nullptr, rout, nullptr, nullptr, 4, 8192, nullptr, &o), UNS);
+    // t = 0 stays a no-op
+    std::memset(&o, 0, sizeof o);
+    o.layout = ARFUSE_LAYOUT_LL;
+    EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 0, 8192, nullptr, &o), OK);
+  }
+
   // auxiliary entries: argument errors and no-op sizes only (no launch)
+  EXPECT(arfuse_quantize_fp4_ll(nullptr, 1, 16, c4, s4, nullptr), INV);
+  EXPECT(arfuse_quantize_fp4_ll(g, 1, 24, c4, s4, nullptr), INV);
+  EXPECT(arfuse_quantize_fp4_ll(g, 1, 16, c4 + 1, s4, nullptr), INV);
+  EXPECT(arfuse_quantize_fp4_ll(g, 1, 64, (uint8_t*)g + 16, s4, nullptr), INV);
+  EXPECT(arfuse_quantize_fp4_ll(g, 0, 16, nullptr, nullptr, nullptr), OK);
+  {
+    const void* ins[2] = {A(19), A(20)};
+    void* outs[2] = {A(21), A(22)};
+    void* bad_outs[2] = {A(21), (char*)A(19) + 16};
+    EXPECT(arfuse_stream_mix(ins, 0, outs, 1, 4, 4096, nullptr), INV);
+    EXPECT(arfuse_stream_mix(ins, 10, outs, 1, 4, 4096, nullptr), INV);
+    EXPECT(arfuse_stream_mix(ins, 2, outs, 4, 4, 4096, nullptr), INV);
+    EXPECT(arfuse_stream_mix(ins, 2, outs, 2, 4, 4104, nullptr), INV);
+    EXPECT(arfuse_stream_mix(ins, 2, bad_outs, 2, 4, 4096, nullptr), INV);
+    EXPECT(arfuse_stream_mix(ins, 2, outs, 2, 4, 65536 + 16, nullptr), UNS);
+    EXPECT(arfuse_stream_mix(nullptr, 2, nullptr, 2, 0, 4096, nullptr), OK);
+  }
   EXPECT(arfuse_quantize_fp4(nullptr, 1, 16, c4, s4, nullptr), INV);
   EXPECT(arfuse_quantize_fp4(g, 1, 24, c4, s4, nullptr), INV);
   EXPECT(arfuse_stream_copy(A(19), A(20), 24, nullptr), INV);

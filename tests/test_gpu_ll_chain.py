@@ -191,9 +191,11 @@ class Chain:
                     assert bad == 0
                     ps.append(p.reshape(self.t, self.d))
                 sets.append(np.stack(ps))
-            return orc().chain(sets, self.ci.residual, self.ci.gamma, self.ci.eps, self.k)
+            return orc().chain(sets, self.ci.residual, self.ci.gamma, self.ci.eps, self.k,
+                               per_call=True)
         src = self.sets if self.sets is not None else self.ci.partials
-        return orc().chain(src, self.ci.residual, self.ci.gamma, self.ci.eps, self.k)
+        return orc().chain(src, self.ci.residual, self.ci.gamma, self.ci.eps, self.k,
+                           per_call=self.sets is not None)
 
 
 def check_chain(ch, ref, what):
@@ -246,8 +248,8 @@ def test_graph_chain(n, t, d, k, per_call, ll):
     (4, 8, 4096, 64, False, False, 2),
 ])
 def test_graph_chain_split_rows(n, t, d, k, per_call, ll, split):
-    """The same chains with split rows: every call advances the workspace's
-    sequence, in eager runs and graph replays alike."""
+    """The same chains with split rows: every call's slices find each other's
+    shares by the call's own token, in eager runs and graph replays alike."""
     ch = Chain(n, t, d, k, seed=40 + n, per_call_sets=per_call, ll=ll, split=split)
     ref = ch.oracle()
     what = "split chain n=%d d=%d k=%d ll=%s split=%d" % (n, d, k, ll, split)
@@ -269,8 +271,10 @@ def test_graph_chain_split_rows(n, t, d, k, per_call, ll, split):
         check_chain(ch, ref, what + " replay %d" % rep)
         ch.enqueue()
         torch.cuda.synchronize()
-    seq = ch.ws.cpu().numpy().view(np.uint32).reshape(t * split, 4)[:, 2]
-    assert np.all(seq == 7 * k), "every call advances every slot once"
+    w = ch.ws.cpu().numpy().view(np.uint32).reshape(t * split, 4)
+    tok = w[:, 2].astype(np.uint64) | (w[:, 3].astype(np.uint64) << np.uint64(32))
+    assert len(set(tok.tolist())) == 1 and int(tok[0]) & (1 << 32), \
+        "every slot carries the last call's token"
 
 
 @pytest.mark.parametrize("n,t,d", [(3, 5, 48), (5, 7, 1040), (6, 3, 8208), (2, 2, 65520),

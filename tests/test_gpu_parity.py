@@ -137,22 +137,30 @@ def test_zero_and_constant_rows():
 
 # ------------------------------------------------ FP4 entry, bit-exact
 
-def quant_gpu(y):
+# The FP4 epilogue comes in two lane geometries: plain and sentinel rows hold
+# 8 contiguous elements per lane, a block in a lane pair (fp4_pair,
+# arfuse_quantize_fp4); LL rows hold 4-element groups, a block in a lane quad
+# (fp4_quad, arfuse_quantize_fp4_ll). Each test runs both.
+GEOMETRIES = pytest.mark.parametrize("ll", [False, True], ids=["pair", "quad"])
+
+
+def quant_gpu(y, ll=False):
     t, d = y.shape
     yd = dev_f32(y)
     codes = torch.empty((t, d // 2), dtype=torch.uint8, device="cuda:0")
     scales = torch.empty((t, d // 16), dtype=torch.uint8, device="cuda:0")
-    arf.arfuse_quantize_fp4(yd, codes, scales)
+    (arf.arfuse_quantize_fp4_ll if ll else arf.arfuse_quantize_fp4)(yd, codes, scales)
     torch.cuda.synchronize()
     return codes.cpu().numpy(), scales.cpu().numpy()
 
 
-def test_quantize_bit_exact_on_oracle_y():
+@GEOMETRIES
+def test_quantize_bit_exact_on_oracle_y(ll):
     orc = __import__("oracle").default()
     ci = si.make_workload("fp4_n4_t64_d8192")
     ref = orc.allreduce_rmsnorm(ci.partials, ci.residual, ci.gamma, ci.eps, fp4=True)
-    note("quantize oracle y32")
-    c, s = quant_gpu(ref["y32"])
+    note("quantize oracle y32 ll=%s" % ll)
+    c, s = quant_gpu(ref["y32"], ll)
     assert np.array_equal(s, ref["scales"])
     assert np.array_equal(c, ref["codes"])
 
@@ -185,36 +193,44 @@ def _tie_blocks():
     return y.reshape(-1, 64)  # 4 blocks per row
 
 
-def test_quantize_bit_exact_near_ties():
+@GEOMETRIES
+def test_quantize_bit_exact_near_ties(ll):
+    """Every value of these blocks lies within 2 ulps of s * (an E2M1
+    decision point), so the hardware conversion's envelope leaves each one
+    open and the exact comparison fallback decides every code."""
     orc = __import__("oracle").default()
     y = _tie_blocks()
     wc, ws = orc.quantize_fp4(y)
-    note("quantize near-tie sweep rows=%d" % y.shape[0])
-    c, s = quant_gpu(y)
+    note("quantize near-tie sweep rows=%d ll=%s" % (y.shape[0], ll))
+    c, s = quant_gpu(y, ll)
     assert np.array_equal(s, ws)
     assert np.array_equal(c, wc)
 
 
-def test_quantize_bit_exact_random_octaves():
+@GEOMETRIES
+def test_quantize_bit_exact_random_octaves(ll):
     orc = __import__("oracle").default()
     rng = np.random.default_rng(12)
     y = (rng.standard_normal((300, 1024)) * np.exp2(rng.uniform(-14, 8, (300, 1)))).astype(np.float32)
     y[::5, ::3] = -0.0
     y[7] = 0
     wc, ws = orc.quantize_fp4(y)
-    note("quantize random octaves")
-    c, s = quant_gpu(y)
+    note("quantize random octaves ll=%s" % ll)
+    c, s = quant_gpu(y, ll)
     assert np.array_equal(s, ws) and np.array_equal(c, wc)
 
 
-def test_quantize_ragged_rows():
+@GEOMETRIES
+def test_quantize_ragged_rows(ll):
+    """Row counts and widths whose blocks leave part of the last workgroup
+    idle (the idle lanes clamp to the last block and store nothing)."""
     orc = __import__("oracle").default()
     rng = np.random.default_rng(13)
-    for (t, d) in [(1, 16), (3, 48), (7, 1040)]:
+    for (t, d) in [(1, 16), (3, 48), (7, 1040), (5, 4112)]:
         y = rng.standard_normal((t, d)).astype(np.float32)
         wc, ws = orc.quantize_fp4(y)
-        note("quantize t=%d d=%d" % (t, d))
-        c, s = quant_gpu(y)
+        note("quantize t=%d d=%d ll=%s" % (t, d, ll))
+        c, s = quant_gpu(y, ll)
         assert np.array_equal(s, ws) and np.array_equal(c, wc)
 
 

@@ -107,7 +107,7 @@ def test_pattern(pattern, layout):
                       out=kw.get("out", True), fp4=kw.get("fp4", False),
                       fp8_inv_scale=kw.get("fp8"), residual_out=kw.get("rout", True))
     note("pattern %s layout %d" % (pattern, layout))
-    extra = dict(status=new_status(), max_polls=1) if layout == SENT else {}
+    extra = dict(status=new_status(), max_polls=1) if layout in (LL, SENT) else {}
     got = run(ci, layout=layout, flag=flag, **kw, **extra)
     if extra:
         assert read_status(extra["status"]) == (0, 0)
@@ -214,9 +214,11 @@ def test_sentinel_reset_refills_slots(n, t, d):
     ro = torch.empty_like(o)
     slots = [torch.full((t, d), 7, dtype=torch.int16, device=DEV) for _ in range(n)]
     note("sentinel reset")
+    st = new_status()
     arf.arfuse_rmsnorm_ex(parts, res, g, float(ci.eps), o, ro, layout=SENT, sentinel=0xFFC1,
-                          reset=slots)
+                          reset=slots, status=st)
     torch.cuda.synchronize()
+    assert read_status(st) == (0, 0)
     for sl in slots:
         assert np.all(sl.cpu().numpy().view(np.uint16) == 0xFFC1)
     ref = orc().allreduce_rmsnorm(ci.partials, ci.residual, ci.gamma, ci.eps)
@@ -233,9 +235,11 @@ def test_sentinel_allreduce_only_with_reset(t):
     ro = torch.empty((t, d), dtype=torch.bfloat16, device=DEV)
     slots = [torch.zeros((t, d), dtype=torch.int16, device=DEV) for _ in range(n)]
     note("sentinel all-reduce only with reset t=%d" % t)
+    st = new_status()
     arf.arfuse_rmsnorm_ex(parts, dev_u16(ci.residual), None, float(ci.eps), None, ro, t=t, d=d,
-                          layout=SENT, reset=slots)
+                          layout=SENT, reset=slots, status=st)
     torch.cuda.synchronize()
+    assert read_status(st) == (0, 0)
     for sl in slots:
         assert np.all(sl.cpu().numpy().view(np.uint16) == arf.ARFUSE_SENTINEL_DEFAULT)
     ref = orc().fused(ci.partials, ci.residual, None, ci.eps)
@@ -313,7 +317,7 @@ def test_sentinel_triple_buffered_chain_in_graph(split):
                                   status=st, reset=[slots[nxt, i] for i in range(n)],
                                   split=split, workspace=ws)
 
-    ref = orc().chain(sets, ci.residual, ci.gamma, ci.eps, k)
+    ref = orc().chain(sets, ci.residual, ci.gamma, ci.eps, k, per_call=True)
     note("sentinel chain split=%d eager" % split)
     enqueue()
     torch.cuda.synchronize()
@@ -375,7 +379,7 @@ def test_streaming_store_instances(pattern, layout):
                       out=kw.get("out", True), fp4=kw.get("fp4", False),
                       fp8_inv_scale=kw.get("fp8"))
     note("streaming stores %s layout %d t=%d d=%d" % (pattern, layout, t, d))
-    extra = dict(status=new_status(), max_polls=1) if layout == SENT else {}
+    extra = dict(status=new_status(), max_polls=1) if layout in (LL, SENT) else {}
     got = run(ci, layout=layout, **kw, **extra)
     if extra:
         assert read_status(extra["status"]) == (0, 0)

@@ -67,7 +67,7 @@ def test_sweep_case(case):
         eff = 1
     note("sweep case %d: n=%d t=%d d=%d layout=%d split=%d (runs %d) %s"
          % (case, n, t, d, layout, split, eff, kw))
-    for _ in range(2):          # the second call exercises the advanced sequence
+    for _ in range(2):          # the second call finds the first call's slots stale
         c.go(**opts)
         check(c.fetch(), ref)
     assert read_status(opts["status"]) == (0, 0, 0)

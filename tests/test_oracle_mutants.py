@@ -99,3 +99,51 @@ def test_mutant_fails_a_pin(name, tmp_path):
             failed.append((pin.__name__, str(e)[:80]))
             break
     assert failed, "mutant %s passed every pin" % name
+
+
+# Planted mistakes in the chained replay (Python, oracle/__init__.py): each
+# replaces Oracle.chain with a plausible wrong version and must fail a pin.
+def _chain_residual_not_handed_on(self, sets, r0, gamma, eps, k, fp4=False, per_call=False):
+    return [self.allreduce_rmsnorm(sets[c] if per_call else sets, r0, gamma, eps, fp4=fp4)
+            for c in range(k)]
+
+
+def _chain_sets_reversed(self, sets, r0, gamma, eps, k, fp4=False, per_call=False):
+    res, out = r0, []
+    for c in range(k):
+        r = self.allreduce_rmsnorm(sets[k - 1 - c] if per_call else sets, res, gamma, eps, fp4=fp4)
+        out.append(r)
+        res = r["residual_out"]
+    return out
+
+
+def _chain_first_set_only(self, sets, r0, gamma, eps, k, fp4=False, per_call=False):
+    res, out = r0, []
+    for c in range(k):
+        r = self.allreduce_rmsnorm(sets[0] if per_call else sets, res, gamma, eps, fp4=fp4)
+        out.append(r)
+        res = r["residual_out"]
+    return out
+
+
+def _chain_one_call_short(self, sets, r0, gamma, eps, k, fp4=False, per_call=False):
+    res, out = r0, []
+    for c in range(k):
+        r = self.allreduce_rmsnorm(sets[c] if per_call else sets, res, gamma, eps, fp4=fp4)
+        out.append(r)
+        if c + 1 < k - 1:
+            res = r["residual_out"]
+    return out
+
+
+CHAIN_MUTANTS = {"residual_not_handed_on": _chain_residual_not_handed_on,
+                 "sets_reversed": _chain_sets_reversed,
+                 "first_set_only": _chain_first_set_only,
+                 "last_hand_off_missing": _chain_one_call_short}
+
+
+@pytest.mark.parametrize("name", sorted(CHAIN_MUTANTS))
+def test_chain_mutant_fails_a_pin(name):
+    broken = type("BrokenChain", (oracle.Oracle,), {"chain": CHAIN_MUTANTS[name]})()
+    with pytest.raises(AssertionError):
+        oracle_pins.pin_chain(broken)
