@@ -12,12 +12,18 @@ served from the 256 MB Infinity Cache.
 `value` is GB/s counted as ((N + 2) reads + 2 writes) x t x d x 2 bytes, the
 counting the workload definition asks for. `roofline.achieved` uses the
 algorithmic bytes instead (N partials + residual + gamma read, residual_out +
-y written). The decode shapes (single token; Llama-3-8B and Llama-3.1-70B
-decode steps as 64- and 160-call hipGraph chains, plain and LL-packed) and
-the FP4 shapes are reported under "extras" as µs per call against the
-measured floor of an empty kernel with the same launch in the same graph.
+y written).
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1]
+The last stdout line is one compact JSON record. Besides the prefill figures
+it carries `decode`: µs per call (p50 of graph replays) of every decode shape
+(single token; the Llama-3-8B and Llama-3.1-70B decode steps as 64- and
+160-call hipGraph chains, plain and LL-packed; the FP4 shapes at t <= 64)
+against the measured floor of an empty kernel with the same launch in a graph
+of the same length, and `prefill_t512`: the single-round prefill calls next to
+a copy of the same byte mix in the same launch shape. Every secondary
+measurement (`--all-extras`) goes to a JSON file, not to stdout.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--all-extras]
 """
 
 from __future__ import annotations
@@ -245,10 +251,16 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
     status = torch.zeros(4, dtype=torch.int32, device=_dev())
     f8 = torch.empty((t, d), dtype=torch.uint8, device=_dev()) if fp8 else None
     slots = [torch.empty_like(res0) for _ in range(n)] if sentinel else None
-    ws = torch.zeros(16 * t * split, dtype=torch.uint8, device=_dev()) if split > 1 else None
-    sx = dict(split=split, workspace=ws)
     epi = ((arf.ARFUSE_EPI_BF16 if out else 0) | (arf.ARFUSE_EPI_FP4 if fp4 else 0)
            | (arf.ARFUSE_EPI_FP8 if fp8 else 0))
+    lay = (arf.ARFUSE_LAYOUT_LL if ll else
+           arf.ARFUSE_LAYOUT_SENTINEL if sentinel else arf.ARFUSE_LAYOUT_PLAIN)
+    # the split that runs (ARFUSE_SPLIT_AUTO: the library's choice for the shape)
+    info = arf.arfuse_query_launch(n, t, d, epi, layout=lay, split=split)
+    eff = int(info.split)
+    ws = (torch.zeros(int(info.workspace_bytes), dtype=torch.uint8, device=_dev())
+          if info.workspace_bytes else None)
+    sx = dict(split=split, workspace=ws)
 
     def enqueue():
         for c in range(k):
@@ -258,7 +270,7 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
                 arf.arfuse_rmsnorm_ex(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales,
                                       layout=arf.ARFUSE_LAYOUT_LL, ll_flag=flags[c], max_polls=4,
                                       status=status, **sx)
-            elif sentinel or fp8 or split > 1 or not norm:
+            elif sentinel or fp8 or split != 0 or not norm:
                 arf.arfuse_rmsnorm_ex(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales,
                                       t=t, d=d, layout=arf.ARFUSE_LAYOUT_SENTINEL if sentinel else 0,
                                       max_polls=4, status=status, reset=slots, fp8_out=f8,
@@ -267,8 +279,6 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
                 arf.arfuse_rmsnorm(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales)
 
     def enqueue_floor():
-        lay = (arf.ARFUSE_LAYOUT_LL if ll else
-               arf.ARFUSE_LAYOUT_SENTINEL if sentinel else arf.ARFUSE_LAYOUT_PLAIN)
         for _ in range(k):
             arf.arfuse_launch_floor(n, t, d, epi, layout=lay, split=split)
 
@@ -285,9 +295,9 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
     st = status.cpu().numpy().view(np.uint32)
     if st[0] != 0:
         raise RuntimeError("arrival reported bad during the benchmark: %s" % st)
-    info = arf.arfuse_query_launch(n, t, d, epi, split=split)
     r = dict(n=n, t=t, d=d, calls=k, layout="ll" if ll else "sentinel" if sentinel else "plain",
-             split=max(1, split), norm=norm,
+             split=eff, split_requested="auto" if split == arf.ARFUSE_SPLIT_AUTO else max(1, split),
+             norm=norm,
              fp4=fp4, fp8=fp8, reset=sentinel, fresh_partials=bool(fresh),
              grid=int(info.grid), block=int(info.block),
              us_per_call_p50=chain["p50"] / k, chain_us_p50=chain["p50"],
@@ -318,6 +328,45 @@ def prefill_gbps(n: int, t: int, d: int, steps: int, warmup: int, fp4=False, out
         r["counted_gbps"] = counted_bytes(n, t, d) / (ms * 1e-3) / 1e9
     del sets
     return r
+
+
+def mix_gbps(n_in: int, n_out: int, t: int, d: int, steps: int, warmup: int, windows: int = 5):
+    """The byte mix of a fused call (n_in planes read, n_out written, bf16
+    [t][d]) without its arithmetic, in the fused call's launch shape
+    (arfuse_stream_mix), with rotating sets like prefill_gbps: the bandwidth
+    ceiling of that call shape."""
+    import torch
+
+    import reduce_residual_rmsnorm_amd as arf
+    P = plane_bytes(t, d)
+    nsets = n_sets_for((n_in + n_out) * P)
+    sets = [([torch.full((P,), 1, dtype=torch.uint8, device=_dev()) for _ in range(n_in)],
+             [torch.empty(P, dtype=torch.uint8, device=_dev()) for _ in range(n_out)])
+            for _ in range(nsets)]
+
+    def call(i):
+        ins, outs = sets[i % nsets]
+        arf.arfuse_stream_mix(ins, outs, t, d)
+
+    per_window = [time_calls(call, steps, warmup if w == 0 else 0) for w in range(windows)]
+    ms = statistics.median(per_window)
+    del sets
+    return dict(n_in=n_in, n_out=n_out, t=t, d=d, nsets=nsets, us_per_call=ms * 1e3,
+                bytes=(n_in + n_out) * P, gbps=(n_in + n_out) * P / (ms * 1e-3) / 1e9)
+
+
+def time_calls_each(fn, steps: int, first: int = 0):
+    """Per-call durations (ms) of `steps` back-to-back calls, from events
+    recorded between them on the launch stream."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        fn(first + i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
 
 def stream_copy_gbps(nbytes: int = 1 << 30, steps: int = 20):
@@ -705,6 +754,130 @@ def run_extras(only=None):
     return out
 
 
+# ------------------------------------------------------------ decode map
+
+# The decode configurations of the workload definition: (label, n, t, d,
+# calls per graph, LL layout, FP4 output). Each is timed with whole rows
+# (one workgroup per row) and with the library's own split choice
+# (ARFUSE_SPLIT_AUTO), against the same-length graph of the empty kernel of
+# the same launch.
+DECODE_MAP = [
+    ("C1_n2_t1_d4096", 2, 1, 4096, 100, False, False),
+    ("C2_n8_t8_d4096_chain64", 8, 8, 4096, 64, False, False),
+    ("C3_n4_t8_d8192_chain160", 4, 8, 8192, 160, False, False),
+    ("C3_n8_t8_d8192_chain160", 8, 8, 8192, 160, False, False),
+    ("C3_n4_t8_d8192_chain160_ll", 4, 8, 8192, 160, True, False),
+    ("C3_n8_t8_d8192_chain160_ll", 8, 8, 8192, 160, True, False),
+    ("C5_n4_t1_d8192_fp4_x100", 4, 1, 8192, 100, False, True),
+    ("C5_n4_t8_d8192_fp4_x100", 4, 8, 8192, 100, False, True),
+    ("C5_n4_t64_d8192_fp4_x100", 4, 64, 8192, 100, False, True),
+]
+
+
+def decode_map(full: dict):
+    """Compact per-config record (µs per call p50, the floor, their ratio;
+    whole rows and the automatic split); the full records go to `full`."""
+    import reduce_residual_rmsnorm_amd as arf
+    out = {}
+    for label, n, t, d, k, ll, fp4 in DECODE_MAP:
+        log("decode %s" % label)
+        kw = dict(ll=ll, fp4=fp4, out=not fp4)
+        whole = decode_chain(n, t, d, k, split=0, **kw)
+        full[label + "_whole"] = whole
+        rec = {"floor_us": round(whole["floor_us_per_node_p50"], 3),
+               "whole_us": round(whole["us_per_call_p50"], 3),
+               "whole_x": round(whole["ratio_to_floor"], 3)}
+        auto = decode_chain(n, t, d, k, split=arf.ARFUSE_SPLIT_AUTO, **kw)
+        if auto["split"] > 1:
+            full[label + "_auto"] = auto
+            rec.update(split=auto["split"], split_floor_us=round(auto["floor_us_per_node_p50"], 3),
+                       split_us=round(auto["us_per_call_p50"], 3),
+                       split_x=round(auto["ratio_to_floor"], 3))
+        else:
+            rec.update(split=1)
+        best = min([rec["whole_x"]] + ([rec["split_x"]] if "split_x" in rec else []))
+        rec["best_x"] = best
+        out[label] = rec
+    return out
+
+
+def prefill_t512(full: dict, steps: int = 100, warmup: int = 10):
+    """The single-round prefill calls (t = 512: one round of workgroups) next
+    to the same byte mix in the same launch shape without the arithmetic."""
+    out = {}
+    log("prefill t=512 (C4)")
+    c4 = prefill_gbps(8, 512, 8192, steps, warmup)
+    log("byte mix of C4 t=512: 9 planes read, 2 written")
+    m4 = mix_gbps(9, 2, 512, 8192, steps, warmup)
+    full["prefill_n8_t512_d8192"], full["mix_9r2w_t512_d8192"] = c4, m4
+    out["C4_n8_t512_d8192"] = {
+        "us": round(c4["us_per_call"], 2), "gbps_counted": round(c4["counted_gbps"], 1),
+        "pct_counted": round(100 * c4["counted_gbps"] / PEAK_HBM_GBPS, 1),
+        "gbps_alg": round(c4["algorithmic_gbps"], 1),
+        "mix_us": round(m4["us_per_call"], 2), "mix_gbps": round(m4["gbps"], 1)}
+    log("prefill t=512 FP4 (C5)")
+    c5 = prefill_gbps(4, 512, 8192, steps, warmup, fp4=True, out=False)
+    log("byte mix of C5 t=512: 5 planes read, 1 written")
+    m5 = mix_gbps(5, 1, 512, 8192, steps, warmup)
+    full["fp4_n4_t512_d8192"], full["mix_5r1w_t512_d8192"] = c5, m5
+    out["C5_n4_t512_d8192_fp4"] = {
+        "us": round(c5["us_per_call"], 2), "gbps_alg": round(c5["algorithmic_gbps"], 1),
+        "mix_us": round(m5["us_per_call"], 2), "mix_gbps": round(m5["gbps"], 1)}
+    return out
+
+
+def reap_children(timeout_s: float = 30.0) -> int:
+    """Wait for (then end) any child process still alive, so the benchmark
+    exits with nothing of its own left running; returns how many there were."""
+    try:
+        import psutil
+    except ImportError:
+        return 0
+    kids = psutil.Process().children(recursive=True)
+    for k in kids:
+        log("child process still alive at exit: pid %d %s" % (k.pid, " ".join(k.cmdline()[:4])))
+    _, alive = psutil.wait_procs(kids, timeout=timeout_s)
+    for k in alive:
+        k.kill()
+    psutil.wait_procs(alive, timeout=5)
+    return len(kids)
+
+
+def bench_record(name, n, t, d, steps, warmup, ms, ms_p50, value, achieved, traffic, cpu,
+                 cpu_all, dec, t512):
+    """The one JSON record bench.py prints last (kept to a few KB: the full
+    records of every measurement go to the extras file)."""
+    if cpu:
+        cpu = dict(cpu, value=round(cpu["value"], 3))
+    return {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms, 6),
+        "ms_per_step_p50": round(ms_p50, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1)/sqrt(N) partials, N(0,1) residual with 0.1% x100 rows, "
+                "U(0.5,1.5) gamma)",
+        "config": {"workload": name, "n_partials": n, "tokens": t, "hidden": d,
+                   "pct_of_peak_counted": round(100 * value / PEAK_HBM_GBPS, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "cpu_baseline_threads": ({"value": round(cpu_all["value"], 2), "unit": "GB/s",
+                                  "cores": cpu_all["cores"]} if cpu_all else None),
+        "decode": dec,
+        "prefill_t512": t512,
+        "kernel_source": source_digest(),
+    }
+
+
 # ------------------------------------------------------------ main
 
 def main(argv=None):
@@ -712,7 +885,12 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-extras", action="store_true", help="only the timed prefill workload")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed prefill workload (no decode map, no t=512 figures)")
+    ap.add_argument("--all-extras", action="store_true",
+                    help="also run every secondary measurement (into --extras-out)")
+    ap.add_argument("--extras-out", default=os.path.join("gpurun_out", "bench_extras.json"),
+                    help="JSON file for the full records of every secondary measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the streaming-copy reference (counter calibration)")
@@ -764,11 +942,23 @@ def main(argv=None):
     ms = time_calls(sets.call, args.steps, args.warmup)
     value = counted_bytes(n, t, d) / (ms * 1e-3) / 1e9
     achieved = (rd + wr) / (ms * 1e-3) / 1e9
-    log("%.2f us/call, %.0f GB/s counted, %.0f GB/s algorithmic" % (ms * 1e3, value, achieved))
+    # a second pass with an event between every call, for the median call
+    each = time_calls_each(sets.call, args.steps, args.warmup + args.steps)
+    ms_p50 = statistics.median(each)
+    log("%.2f us/call (p50 %.2f), %.0f GB/s counted, %.0f GB/s algorithmic"
+        % (ms * 1e3, ms_p50 * 1e3, value, achieved))
     del sets
     torch.cuda.empty_cache()
 
-    extras = {} if args.no_extras else run_extras()
+    full = {}
+    dec = t512 = None
+    if not args.no_extras:
+        dec = decode_map(full)
+        torch.cuda.empty_cache()
+        t512 = prefill_t512(full)
+        torch.cuda.empty_cache()
+        if args.all_extras:
+            full.update(run_extras())
     cpu = cpu_all = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -778,38 +968,23 @@ def main(argv=None):
         log("cpu baseline (oracle), rows on %d threads" % threads)
         cpu_all = cpu_baseline_threads(ci, threads)
 
-    traffic = recorded_traffic(name)
-    line = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "dtype_detail": "bf16 storage; fp32 rank-ordered sum and residual add; fp64 sum of squares and inverse RMS; fp32 scaling",
-        "data": "synthetic (seeded N(0,1)/sqrt(N) partials, N(0,1) residual with 0.1% x100 rows, "
-                "U(0.5,1.5) gamma)",
-        "config": {"workload": name, "n_partials": n, "tokens": t, "hidden": d,
-                   "pct_of_peak_counted": round(100 * value / PEAK_HBM_GBPS, 1),
-                   "bytes_counted_per_step": counted_bytes(n, t, d),
-                   "bytes_algorithmic_per_step": rd + wr,
-                   "launch": {"grid": int(info.grid), "block": int(info.block),
-                              "vpt": int(info.vpt),
-                              "stream_stores": int(info.stream_stores)}},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic},
-        "cpu_baseline": cpu,
-        "cpu_baseline_threads": cpu_all,
-        "kernel_source": source_digest(),
-        "extras": extras,
-    }
-    print(json.dumps(line), flush=True)
+    if full:
+        try:
+            os.makedirs(os.path.dirname(os.path.abspath(args.extras_out)), exist_ok=True)
+            with open(args.extras_out, "w") as f:
+                json.dump(dict(kernel_source=source_digest(), records=full), f, indent=1)
+            log("full records written to %s" % args.extras_out)
+        except OSError as e:
+            log("could not write %s: %s" % (args.extras_out, e))
+    for label, rec in (dec or {}).items():
+        log("decode %s: %s" % (label, json.dumps(rec)))
+
+    line = bench_record(name, n, t, d, args.steps, args.warmup, ms, ms_p50, value, achieved,
+                        recorded_traffic(name), cpu, cpu_all, dec, t512)
+    nkids = reap_children()
+    if nkids:
+        line["children_reaped"] = nkids
+    print(json.dumps(line, separators=(",", ":")), flush=True)
     return 0
 
 

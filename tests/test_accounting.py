@@ -96,3 +96,37 @@ def test_rotation_defeats_infinity_cache(call_bytes, sets):
 def test_bench_refuses_more_than_one_gpu(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_bench_record_is_compact_and_complete():
+    """The last stdout line of bench.py stays a few KB even with every decode
+    configuration, the t = 512 figures and both CPU baselines in it (a
+    collector that keeps only the tail of stdout must get all of it)."""
+    dec = {}
+    for label, *_ in bench.DECODE_MAP:
+        dec[label] = {"floor_us": 1.604, "whole_us": 7.512, "whole_x": 4.683, "split": 8,
+                      "split_floor_us": 1.655, "split_us": 4.281, "split_x": 2.587, "best_x": 2.587}
+    t512 = {"C4_n8_t512_d8192": {"us": 16.94, "gbps_counted": 5943.1, "pct_counted": 74.3,
+                                 "gbps_alg": 5449.0, "mix_us": 15.33, "mix_gbps": 6021.4},
+            "C5_n4_t512_d8192_fp4": {"us": 12.56, "gbps_alg": 4197.3, "mix_us": 9.12,
+                                     "mix_gbps": 5519.9}}
+    cpu = {"value": 0.904123, "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": "14 full calls of n=8 t=4096 d=8192 on one host thread (median 0.891 s/call; "
+                     "host AMD EPYC 9575F 64-Core Processor)"}
+    line = bench.bench_record("prefill_n8_t4096_d8192", 8, 4096, 8192, 20, 5, 0.11712, 0.11698,
+                              6876.2, 6303.3, 738396486, cpu,
+                              {"value": 13.41, "cores": 16}, dec, t512)
+    text = json.dumps(line, separators=(",", ":"))
+    assert len(text) < 3072, len(text)
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"):
+        assert key in line, key
+    assert line["config"]["workload"] == "prefill_n8_t4096_d8192"
+    assert set(line["roofline"]) == {"bound", "achieved", "peak", "unit", "frac", "traffic"}
+    assert {"value", "unit", "cores", "kind", "sample"} <= set(line["cpu_baseline"])
+    # every decode configuration of the workload definition is in the map
+    names = {lbl for lbl, *_ in bench.DECODE_MAP}
+    assert set(line["decode"]) == names
+    for want in ("C1_", "C2_", "C3_n4", "C3_n8", "_ll", "C5_n4_t1_", "C5_n4_t8_", "C5_n4_t64_"):
+        assert any(want in x for x in names), want
