@@ -51,7 +51,8 @@
  *  - Pointers marked (device) are HIP device pointers; (host) are host memory.
  *  - bf16 tensors are row-major [t][d] arrays of 16-bit bfloat16.
  *  - The caller owns every buffer. The library allocates no memory, keeps no
- *    pointer after it returns and holds no global state; calls are reentrant.
+ *    pointer after it returns and holds no global state, apart from the
+ *    static exchange slots of arfuse_rmsnorm_noalloc; calls are reentrant.
  *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
  *    work; they never synchronize, so they are legal under stream capture.
  *  - Argument errors are returned before anything is enqueued. A failed
@@ -286,6 +287,33 @@ int arfuse_rmsnorm_ex(const void* const* partials, int n_partials, const void* r
                       const float* gamma, float eps, void* out, void* residual_out,
                       uint8_t* fp4_out, uint8_t* fp4_scales, int64_t t, int64_t d,
                       void* stream, const arfuse_opts* opts);
+
+/*
+ * arfuse_rmsnorm_noalloc — arfuse_rmsnorm_ex for callers that cannot
+ * allocate device memory or be handed a workspace: code under stream or
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Split rows exchange their sums of squares through a static array of
+ * ARFUSE_NOALLOC_SLOTS 16-byte slots (4 KiB) inside the library instead of
+ * opts->workspace, which must be NULL (else ARFUSE_ERR_INVALID_ARG). Every
+ * split the library accepts fits it (t * split <= ARFUSE_MAX_SPLIT_BLOCKS;
+ * larger requests are ARFUSE_ERR_UNSUPPORTED, as for arfuse_rmsnorm_ex).
+ * Each GPU the library runs on holds its own copy of the array until the
+ * process ends; the first call on a device (any call, t == 0 included) looks
+ * up its address there once, with no allocation and nothing enqueued, so a
+ * caller that captures can make a t == 0 call on that device beforehand.
+ * The slots are never cleared and need not be: each call tags them with a
+ * token of its own kernel dispatch. All calls on one GPU share the array,
+ * so calls that overlap in time on one GPU (concurrent streams) race and
+ * their split rows' outputs are unspecified; calls ordered on one stream,
+ * or otherwise serialized, do not. Arguments, outputs, the status word
+ * rule and errors are otherwise those of arfuse_rmsnorm_ex, and the results
+ * are the same bits.
+ */
+#define ARFUSE_NOALLOC_SLOTS ARFUSE_MAX_SPLIT_BLOCKS
+int arfuse_rmsnorm_noalloc(const void* const* partials, int n_partials, const void* residual,
+                           const float* gamma, float eps, void* out, void* residual_out,
+                           uint8_t* fp4_out, uint8_t* fp4_scales, int64_t t, int64_t d,
+                           void* stream, const arfuse_opts* opts);
 
 /*
  * arfuse_quantize_fp4 — the FP4 epilogue alone, on fp32 y [t][d] (device,

@@ -33,9 +33,11 @@ ARFUSE_MAX_POLLS = 1 << 20
 ARFUSE_MAX_SPLIT = 8
 ARFUSE_MAX_SPLIT_BLOCKS = 256
 ARFUSE_SPLIT_AUTO = 0xFFFFFFFF
+ARFUSE_NOALLOC_SLOTS = ARFUSE_MAX_SPLIT_BLOCKS
 
 # The exported functions, as declared in include/arfuse.h.
-EXPORTED = ("arfuse_rmsnorm", "arfuse_rmsnorm_ex", "arfuse_quantize_fp4", "arfuse_quantize_fp4_ll",
+EXPORTED = ("arfuse_rmsnorm", "arfuse_rmsnorm_ex", "arfuse_rmsnorm_noalloc",
+            "arfuse_quantize_fp4", "arfuse_quantize_fp4_ll",
             "arfuse_query_launch", "arfuse_launch_floor", "arfuse_stream_copy", "arfuse_stream_mix",
             "arfuse_round_bf16", "arfuse_round_fp8", "arfuse_round_fp4",
             "arfuse_status_string", "arfuse_version")
@@ -89,6 +91,8 @@ def _load(path: str = LIB_PATH):
     lib.arfuse_rmsnorm.restype = I
     lib.arfuse_rmsnorm_ex.argtypes = common + [ctypes.POINTER(arfuse_opts)]
     lib.arfuse_rmsnorm_ex.restype = I
+    lib.arfuse_rmsnorm_noalloc.argtypes = common + [ctypes.POINTER(arfuse_opts)]
+    lib.arfuse_rmsnorm_noalloc.restype = I
     lib.arfuse_quantize_fp4.argtypes = [P, I64, I64, P, P, P]
     lib.arfuse_quantize_fp4.restype = I
     lib.arfuse_quantize_fp4_ll.argtypes = [P, I64, I64, P, P, P]
@@ -258,6 +262,25 @@ def arfuse_rmsnorm_ex(partials: Sequence, residual, gamma, eps: float, out, resi
                                b["out"], b["residual_out"], b["fp4_out"], b["fp4_scales"],
                                t, d, _stream(stream), ctypes.byref(o))
     _check(rc, "arfuse_rmsnorm_ex")
+
+
+def arfuse_rmsnorm_noalloc(partials: Sequence, residual, gamma, eps: float, out, residual_out,
+                           fp4_out=None, fp4_scales=None, stream=None, t=None, d=None, *,
+                           layout=ARFUSE_LAYOUT_PLAIN, ll_flag=0, max_polls=0, status=None,
+                           block_threads=0, vpt=0, sentinel=0, reset=None, fp8_out=None,
+                           fp8_inv_scale=1.0, split=0) -> None:
+    """arfuse_rmsnorm_ex without a workspace: split rows exchange through the
+    library's static slots (for callers that cannot allocate); see
+    arfuse_rmsnorm_noalloc in include/arfuse.h."""
+    t, d = _td(residual, t, d)
+    b = _call_buffers(partials, residual, gamma, out, residual_out, fp4_out, fp4_scales, t, d,
+                      layout=layout, fp8_out=fp8_out, status=status, reset=reset)
+    o = _opts(layout, ll_flag, max_polls, b["status"], block_threads, vpt, sentinel, b["reset"],
+              b["fp8_out"], fp8_inv_scale, split, None)
+    rc = lib.arfuse_rmsnorm_noalloc(b["arr"], len(partials), b["residual"], b["gamma"],
+                                    float(eps), b["out"], b["residual_out"], b["fp4_out"],
+                                    b["fp4_scales"], t, d, _stream(stream), ctypes.byref(o))
+    _check(rc, "arfuse_rmsnorm_noalloc")
 
 
 def arfuse_quantize_fp4(y, codes, scales, stream=None, t=None, d=None) -> None:

@@ -40,6 +40,9 @@
 //    s * threshold where the envelope leaves a decision open (see
 //    e2m1_envelope and e2m1_two).
 
+#include <cstring>
+#include <mutex>
+
 #include "arfuse_device.hpp"
 
 namespace arfuse_detail {
@@ -468,6 +471,50 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
   return launch_status(e);
 }
 
+// ------------------------------------------------------------ allocation-free calls
+
+// The exchange slots of arfuse_rmsnorm_noalloc: one 16-byte slot per
+// workgroup a split call may launch (t * split <= ARFUSE_MAX_SPLIT_BLOCKS),
+// 4 KiB. Each GPU the library runs on holds its own copy from the library's
+// load until the process ends. Host code never uses this name as an address
+// (on the host it names a stand-in, not device memory): the device address
+// is looked up per device with hipGetSymbolAddress (scratch_on).
+constexpr int kScratchSlots = ARFUSE_MAX_SPLIT_BLOCKS;
+static __device__ __align__(256) u32x4 scratch[kScratchSlots];
+
+// Device address of `scratch` per device, found once (with that device
+// current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+// The device address of `scratch` on the device `stream` belongs to (the
+// current device for the null stream). Allocates nothing.
+int scratch_on(hipStream_t stream, void** addr) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return launch_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return ARFUSE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return launch_status(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return launch_status(e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return launch_status(e);
+    if (!p) return ARFUSE_ERR_LAUNCH;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return ARFUSE_OK;
+}
+
 }  // namespace
 }  // namespace arfuse_detail
 
@@ -488,6 +535,28 @@ int arfuse_rmsnorm_ex(const void* const* partials, int n_partials, const void* r
                       const arfuse_opts* opts) {
   return rmsnorm_impl(partials, n_partials, residual, gamma, eps, out, residual_out, fp4_out,
                       fp4_scales, t, d, stream, opts);
+}
+
+int arfuse_rmsnorm_noalloc(const void* const* partials, int n_partials, const void* residual,
+                           const float* gamma, float eps, void* out, void* residual_out,
+                           uint8_t* fp4_out, uint8_t* fp4_scales, int64_t t, int64_t d,
+                           void* stream, const arfuse_opts* opts) {
+  // the library's static slots stand in for the caller's workspace
+  if (opts && opts->workspace) return ARFUSE_ERR_INVALID_ARG;
+  void* slots = nullptr;
+  const int rc = scratch_on((hipStream_t)stream, &slots);
+  if (rc) return rc;
+  arfuse_opts o;
+  if (opts)
+    o = *opts;
+  else
+    memset(&o, 0, sizeof o);
+  o.workspace = slots;
+  // every split the library launches fits the slots: t * split is capped at
+  // ARFUSE_MAX_SPLIT_BLOCKS, and rmsnorm_impl refuses a larger t * split
+  static_assert(kScratchSlots >= ARFUSE_MAX_SPLIT_BLOCKS, "scratch smaller than a split call");
+  return rmsnorm_impl(partials, n_partials, residual, gamma, eps, out, residual_out, fp4_out,
+                      fp4_scales, t, d, stream, &o);
 }
 
 int arfuse_quantize_fp4(const float* y, int64_t t, int64_t d, uint8_t* codes, uint8_t* scales,

@@ -402,3 +402,18 @@ def test_query_launch_reports_streaming_stores():
     assert q(8, 4096, 8192, layout=arf.ARFUSE_LAYOUT_SENTINEL).stream_stores == 1
     assert q(8, 8, 8192, split=4).stream_stores == 0
     assert q(8, 0, 8192).stream_stores == 0
+
+
+def test_noalloc_refuses_a_workspace():
+    """The allocation-free entry keeps the split exchange in the library's
+    own static slots: a caller workspace is an argument error, returned
+    before anything else happens (no device lookup, nothing enqueued)."""
+    ws = spaced(40)
+    o = arf._opts(split=4, workspace=ws, status=spaced(30))
+    parts = [spaced(i) for i in range(4)]
+    arr = (ctypes.c_void_p * 4)(*parts)
+    for t in (0, T):
+        rc = arf.lib.arfuse_rmsnorm_noalloc(arr, 4, spaced(8), spaced(9), 1e-5, spaced(10),
+                                            spaced(11), None, None, t, 8192, None, ctypes.byref(o))
+        assert rc == arf.ARFUSE_ERR_INVALID_ARG
+    assert arf.ARFUSE_NOALLOC_SLOTS == arf.ARFUSE_MAX_SPLIT_BLOCKS == 256

@@ -187,6 +187,14 @@ int main() {
     EXPECT(arfuse_rmsnorm_ex(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 0, 8192, nullptr, &o), OK);
   }
 
+  // the allocation-free entry refuses a caller workspace before anything else
+  std::memset(&o, 0, sizeof o);
+  o.split = 4;
+  o.workspace = A(17);
+  o.status = (arfuse_ll_status*)A(18);
+  EXPECT(arfuse_rmsnorm_noalloc(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 4, 8192, nullptr, &o), INV);
+  EXPECT(arfuse_rmsnorm_noalloc(parts, 2, res, g, 1e-5f, out, rout, nullptr, nullptr, 0, 8192, nullptr, &o), INV);
+
   // auxiliary entries: argument errors and no-op sizes only (no launch)
   EXPECT(arfuse_quantize_fp4_ll(nullptr, 1, 16, c4, s4, nullptr), INV);
   EXPECT(arfuse_quantize_fp4_ll(g, 1, 24, c4, s4, nullptr), INV);
