@@ -192,9 +192,13 @@ typedef struct {
                                  448), 16-byte aligned; or NULL */
   float fp8_inv_scale;        /* per-tensor reciprocal FP8 scale, finite */
   uint32_t reserved2;         /* must be 0 */
-  void* workspace;            /* split rows: (device) t * split 16-byte slots,
-                                 16-byte aligned (arfuse_query_launch gives
-                                 the size). Each slice tags its slot with a
+  void* workspace;            /* split rows: (device) 256 bytes per row
+                                 position, t rounded up to a multiple of 8
+                                 (two 128-byte lines of slots per row;
+                                 arfuse_query_launch gives the size),
+                                 16-byte aligned (128-byte alignment keeps
+                                 each row's slots in lines of their own, the
+                                 fast case). Each slice tags its slot with a
                                  token of the kernel dispatch (the dispatch's
                                  index in its hardware queue and the queue),
                                  so any earlier contents read as "not yet
@@ -206,9 +210,11 @@ typedef struct {
 
 /* The launch the library would use for a call. */
 typedef struct {
-  int64_t grid;         /* workgroups: split per token row, plus, in the
-                           sentinel layout with a reset set and t <= 128,
-                           the blocks that write the reset */
+  int64_t grid;         /* workgroups: t (one per row), or with split rows
+                           split times t rounded up to a multiple of 8 (the
+                           rows past t are padding that exits at once), plus,
+                           in the sentinel layout with a reset set and
+                           t <= 128, the blocks that write the reset */
   int32_t block;        /* threads per workgroup */
   int32_t vpt;          /* 16-byte vectors per thread per partial */
   int32_t split;        /* workgroups per row (1 unless opts->split > 1,
@@ -268,9 +274,11 @@ int arfuse_rmsnorm(const void* const* partials, int n_partials, const void* resi
  * spin loop). opts->fp8_out requests the FP8 output.
  *
  * opts->split > 1 divides every row's columns between that many workgroups
- * (on different CUs). Each computes its columns' share of the sum of squares,
- * writes it with its dispatch's token to its slot of opts->workspace and
- * waits (bounded) for the row's other slots to carry the same token; the shares
+ * (on different CUs of one XCD where the workgroups of a launch are placed on
+ * the XCDs in turn: a row's slices are launched 8k workgroups apart). Each
+ * computes its columns' share of the sum of squares, writes it with its
+ * dispatch's token to its slot of opts->workspace and waits (bounded) for the
+ * row's other slots to carry the same token; the shares
  * are added in slice order, so the result is deterministic (it may differ in
  * the last bits from the unsplit call, whose sum runs in another order).
  * residual_out, the FP4 and the FP8 outputs are produced per slice exactly as
@@ -293,7 +301,7 @@ int arfuse_rmsnorm_ex(const void* const* partials, int n_partials, const void* r
  * allocate device memory or be handed a workspace: code under stream or
  * graph capture, tight serving loops, harnesses that forbid allocation.
  * Split rows exchange their sums of squares through a static array of
- * ARFUSE_NOALLOC_SLOTS 16-byte slots (4 KiB) inside the library instead of
+ * ARFUSE_NOALLOC_BYTES (32 KiB) inside the library instead of
  * opts->workspace, which must be NULL (else ARFUSE_ERR_INVALID_ARG). Every
  * split the library accepts fits it (t * split <= ARFUSE_MAX_SPLIT_BLOCKS;
  * larger requests are ARFUSE_ERR_UNSUPPORTED, as for arfuse_rmsnorm_ex).
@@ -309,7 +317,7 @@ int arfuse_rmsnorm_ex(const void* const* partials, int n_partials, const void* r
  * rule and errors are otherwise those of arfuse_rmsnorm_ex, and the results
  * are the same bits.
  */
-#define ARFUSE_NOALLOC_SLOTS ARFUSE_MAX_SPLIT_BLOCKS
+#define ARFUSE_NOALLOC_BYTES 32768
 int arfuse_rmsnorm_noalloc(const void* const* partials, int n_partials, const void* residual,
                            const float* gamma, float eps, void* out, void* residual_out,
                            uint8_t* fp4_out, uint8_t* fp4_scales, int64_t t, int64_t d,

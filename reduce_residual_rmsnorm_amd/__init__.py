@@ -33,7 +33,7 @@ ARFUSE_MAX_POLLS = 1 << 20
 ARFUSE_MAX_SPLIT = 8
 ARFUSE_MAX_SPLIT_BLOCKS = 256
 ARFUSE_SPLIT_AUTO = 0xFFFFFFFF
-ARFUSE_NOALLOC_SLOTS = ARFUSE_MAX_SPLIT_BLOCKS
+ARFUSE_NOALLOC_BYTES = 32768
 
 # The exported functions, as declared in include/arfuse.h.
 EXPORTED = ("arfuse_rmsnorm", "arfuse_rmsnorm_ex", "arfuse_rmsnorm_noalloc",
@@ -171,8 +171,10 @@ def _call_buffers(partials, residual, gamma, out, residual_out, fp4_out, fp4_sca
         fp4_scales=_buf(fp4_scales, t * d // 16, "fp4_scales"),
         fp8_out=_buf(fp8_out, t * d, "fp8_out"),
         status=_buf(status, 16, "status"),
-        # an unsplit call never touches the workspace
-        workspace=_buf(workspace, 16 * t * int(split) if int(split) > 1 else 0, "workspace"),
+        # an unsplit call never touches the workspace; a split one uses 256
+        # bytes per row position (t rounded up to a multiple of 8)
+        workspace=_buf(workspace, 256 * ((t + 7) // 8 * 8) if int(split) > 1 else 0,
+                       "workspace"),
         reset=None if reset is None else [_buf(r, plane, "reset[%d]" % i)
                                           for i, r in enumerate(reset)])
 
@@ -239,7 +241,8 @@ def arfuse_rmsnorm_ex(partials: Sequence, residual, gamma, eps: float, out, resi
     residual and gamma may be None (the no-residual and all-reduce-only
     patterns); then pass t and d explicitly. split > 1 divides each row
     between that many workgroups, which exchange their sums of squares
-    through `workspace` (t * split 16-byte slots, zeroed before first use);
+    through `workspace` (256 bytes per row position, t rounded up to a
+    multiple of 8; never needs clearing);
     ARFUSE_SPLIT_AUTO lets the library choose (arfuse_query_launch tells
     the choice and the workspace size)."""
     t, d = _td(residual, t, d)

@@ -311,6 +311,18 @@ int auto_split_log2(int n, int64_t t, int64_t d, bool ll, bool norm) {
   return lg;
 }
 
+// Split rows launch their slices at row positions 0..prows-1, prows being t
+// rounded up to a multiple of 8, so that slice b / prows of row b % prows
+// shares b mod 8 (its XCD) with the row's other slices; rows past t are
+// padding. With t * split <= ARFUSE_MAX_SPLIT_BLOCKS and split <= 8, the
+// padded launch prows * split fits the same cap (256 / split is a multiple of
+// 8).
+int64_t split_rows(int64_t t, int lg) { return lg ? (t + 7) / 8 * 8 : t; }
+
+// Bytes of a split call's exchange slots: two regions of one 128-byte line
+// per row position (at most 128 positions: 32 KiB).
+int64_t split_ws_bytes(int64_t t, int lg) { return lg ? split_rows(t, lg) * 256 : 0; }
+
 // Split rows: the validated number of workgroups per row, as its log2 (0 when
 // a row is one workgroup). Every workgroup of a split row must be resident at
 // once, hence the cap on t * split.
@@ -399,7 +411,9 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
     outs[nout++] = range_of(fp4_scales, t * d / 16);
   }
   if (fp8_out) outs[nout++] = range_of(fp8_out, t * d);
-  if (workspace) outs[nout++] = range_of(workspace, (t << lg) * 16);
+  const int64_t prows = split_rows(t, lg);
+  if ((prows << lg) > ARFUSE_MAX_SPLIT_BLOCKS && lg) return ARFUSE_ERR_UNSUPPORTED;
+  if (workspace) outs[nout++] = range_of(workspace, split_ws_bytes(t, lg));
   arfuse_ll_status* status = opts ? opts->status : nullptr;
   if (status) {  // written by device atomics: 8-byte aligned, shared with nothing
     if ((uintptr_t)status & 7u) return ARFUSE_ERR_INVALID_ARG;
@@ -460,27 +474,28 @@ int rmsnorm_impl(const void* const* partials, int n, const void* residual, const
   a.split_log2 = (uint32_t)lg;
   a.ds8 = (uint32_t)((d / 8) >> lg);
   a.ws = (u32x4*)workspace;
+  a.prows = (uint32_t)prows;
   a.plane_vecs = (uint32_t)(t * d / 8);  // only read by reset blocks: t <= 128
   a.reset_bpp = (uint32_t)((t * d / 8 + block - 1) / block);
 
   const void* fn = (const void*)select_row_kernel(n, vpt, layout, epi, row_kind(t, lg, vpt, layout));
   if (!fn) return ARFUSE_ERR_UNSUPPORTED;
   void* args[] = {&a};
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)((t << lg) + extra)), dim3((unsigned)block), args, 0,
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)((prows << lg) + extra)), dim3((unsigned)block), args, 0,
                                  (hipStream_t)stream);
   return launch_status(e);
 }
 
 // ------------------------------------------------------------ allocation-free calls
 
-// The exchange slots of arfuse_rmsnorm_noalloc: one 16-byte slot per
-// workgroup a split call may launch (t * split <= ARFUSE_MAX_SPLIT_BLOCKS),
-// 4 KiB. Each GPU the library runs on holds its own copy from the library's
-// load until the process ends. Host code never uses this name as an address
-// (on the host it names a stand-in, not device memory): the device address
-// is looked up per device with hipGetSymbolAddress (scratch_on).
-constexpr int kScratchSlots = ARFUSE_MAX_SPLIT_BLOCKS;
-static __device__ __align__(256) u32x4 scratch[kScratchSlots];
+// The exchange slots of arfuse_rmsnorm_noalloc: the largest split call's
+// (128 row positions, two 128-byte lines each), 32 KiB. Each GPU the library
+// runs on holds its own copy from the library's load until the process ends.
+// Host code never uses this name as an address (on the host it names a
+// stand-in, not device memory): the device address is looked up per device
+// with hipGetSymbolAddress (scratch_on).
+constexpr int64_t kScratchBytes = ARFUSE_NOALLOC_BYTES;
+static __device__ __align__(256) u32x4 scratch[kScratchBytes / 16];
 
 // Device address of `scratch` per device, found once (with that device
 // current) and kept.
@@ -552,9 +567,10 @@ int arfuse_rmsnorm_noalloc(const void* const* partials, int n_partials, const vo
   else
     memset(&o, 0, sizeof o);
   o.workspace = slots;
-  // every split the library launches fits the slots: t * split is capped at
-  // ARFUSE_MAX_SPLIT_BLOCKS, and rmsnorm_impl refuses a larger t * split
-  static_assert(kScratchSlots >= ARFUSE_MAX_SPLIT_BLOCKS, "scratch smaller than a split call");
+  // every split the library launches fits the slots: a split row has at
+  // least 2 workgroups and t * split <= ARFUSE_MAX_SPLIT_BLOCKS, so at most
+  // ARFUSE_MAX_SPLIT_BLOCKS / 2 row positions of 256 bytes
+  static_assert(kScratchBytes >= ARFUSE_MAX_SPLIT_BLOCKS / 2 * 256, "scratch smaller than a split call");
   return rmsnorm_impl(partials, n_partials, residual, gamma, eps, out, residual_out, fp4_out,
                       fp4_scales, t, d, stream, &o);
 }
@@ -658,12 +674,12 @@ int arfuse_query_launch(int n_partials, int64_t t, int64_t d, int epilogue,
   rc = row_launch(d, lg, opts, &block, &vpt);
   if (rc) return rc;
   const bool reset = opts && opts->layout == ARFUSE_LAYOUT_SENTINEL && opts->reset;
-  info->grid = (t << lg) + reset_blocks(n_partials, t, d, block, reset);
+  info->grid = (split_rows(t, lg) << lg) + reset_blocks(n_partials, t, d, block, reset);
   info->block = block;
   info->vpt = vpt;
   info->split = 1 << lg;
   info->stream_stores = row_kind(t, lg, vpt, opts ? opts->layout : ARFUSE_LAYOUT_PLAIN) == kRowStream;
-  info->workspace_bytes = lg ? (t << lg) * 16 : 0;
+  info->workspace_bytes = split_ws_bytes(t, lg);
   return ARFUSE_OK;
 }
 
@@ -679,7 +695,7 @@ int arfuse_launch_floor(int n_partials, int64_t t, int64_t d, int epilogue,
   if (rc) return rc;
   if (t == 0) return ARFUSE_OK;
   const bool reset = opts && opts->layout == ARFUSE_LAYOUT_SENTINEL && opts->reset;
-  const int64_t grid = (t << lg) + reset_blocks(n_partials, t, d, block, reset);
+  const int64_t grid = (split_rows(t, lg) << lg) + reset_blocks(n_partials, t, d, block, reset);
   RowArgs a = {};
   void* args[] = {&a};
   hipError_t e = hipLaunchKernel((const void*)floor_kernel, dim3((unsigned)grid), dim3((unsigned)block),

@@ -44,13 +44,18 @@ struct RowArgs {
   uint32_t rows;        // t
   uint32_t plane_vecs;  // 16-byte vectors per slot plane (t * d / 8)
   uint32_t reset_bpp;   // reset blocks per plane (plane_vecs / block, rounded up)
-  // split rows: workgroup b < rows << split_log2 takes column slice
-  // b & (split - 1) of row b >> split_log2; the slice's workgroups exchange
-  // their sums of squares through ws (slot b: {fp64 partial, 64-bit token of
-  // the dispatch})
+  // split rows: the launch has prows = rows rounded up to a multiple of 8
+  // row positions per slice; workgroup b < prows << split_log2 takes column
+  // slice b / prows of row b % prows (rows past `rows` are padding and exit),
+  // so a row's workgroups share b mod 8, i.e. one XCD. They exchange their
+  // sums of squares through ws: two regions of prows 128-byte lines, line r
+  // holding row r's slots (slot = {fp64 share, 64-bit token of the
+  // dispatch}), the first written and read through the L2, the second
+  // written through to memory
   uint32_t split_log2;  // 0: one workgroup per row
   uint32_t ds8;         // 16-byte vectors per slice (d8 >> split_log2)
   u32x4* ws;
+  uint32_t prows;       // split rows: rows rounded up to a multiple of 8
 };
 
 // RowArgs.flags. These features do not change the kernel's shape, so they are
@@ -277,6 +282,23 @@ __device__ __forceinline__ bool ll_ok(u32x4 w, uint64_t flag) {
 // the caches (sc0 sc1, the same policy as reread16), one instruction, so a
 // reader sees either the old word or all of the new one.
 __device__ __forceinline__ void store16_through(char* base, uint32_t bytes, uint32_t off, u32x4 v);
+
+// Re-read through the L2 (sc0: past the L1 only), for a partner workgroup on
+// the same XCD, which shares that L2.
+constexpr int kRereadL2Policy = (int)0x80000001u;
+__device__ __forceinline__ u32x4 reread16_l2(const char* row, uint32_t row_bytes, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, (int)row_bytes, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kRereadL2Policy);
+}
+
+// Store of a 16-byte word for partners on the same XCD (sc0: through the L1
+// into the shared L2).
+__device__ __forceinline__ void store16_l2(char* base, uint32_t bytes, uint32_t off, u32x4 v) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0x1);
+}
 
 // Re-read of a 16-byte vector another agent may still be writing: a buffer
 // load through a descriptor of the row (scalar registers) at the lane's
@@ -608,12 +630,13 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     asm volatile("" ::"s"(a.part[0]), "s"(a.part[1]), "s"(a.part[2]), "s"(a.part[3]),
                  "s"(a.part[4]), "s"(a.part[5]), "s"(a.part[6]), "s"(a.part[7]), "s"(a.residual),
                  "s"(a.gamma), "s"(a.out), "s"(a.residual_out), "s"(a.d8), "s"(a.flags),
-                 "s"(a.rows), "s"(a.split_log2), "s"(a.ds8));
+                 "s"(a.rows), "s"(a.split_log2), "s"(a.ds8), "s"(a.prows));
   }
   // split instances are launched with split_log2 >= 1; the others fold every
   // slice computation away
   const uint32_t lg = SPLIT ? a.split_log2 : 0u;
-  const uint32_t row_blocks = a.rows << lg;
+  const uint32_t prows = SPLIT ? a.prows : a.rows;  // row positions per slice
+  const uint32_t row_blocks = prows << lg;
   if constexpr (SENT) {
     // a reset block (only launched when the rows are few): refill one chunk
     // of one slot plane of the set a later call reuses, a vector per lane,
@@ -627,8 +650,14 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     }
   }
   // this workgroup's columns: the whole row, or one slice of a split row
-  const uint32_t row = blockIdx.x >> lg;
-  const uint32_t slice = blockIdx.x & ((1u << lg) - 1u);
+  // (row b mod prows, so every slice of a row has the same b mod 8: the
+  // workgroups of a launch go to the XCDs in turn, b mod 8, and a row's
+  // slices then share an L2 for their exchange)
+  const uint32_t row = SPLIT ? blockIdx.x % prows : blockIdx.x;
+  const uint32_t slice = SPLIT ? blockIdx.x / prows : 0u;
+  if constexpr (SPLIT) {
+    if (row >= a.rows) return;  // padding row position
+  }
   const uint32_t d = (uint32_t)(a.d8 * 8);  // the row width: the mean's divisor
   const uint32_t ds = SPLIT ? a.ds8 * 8 : d;  // the columns this workgroup handles
   const int64_t rb = (int64_t)row * d + (int64_t)slice * ds;  // its first element
@@ -890,23 +919,37 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     // dispatch's token, then lanes 0..split-1 of wave 0 wait (bounded) for
     // every partner slot to carry the same token; the partials are added in
     // slice order, so every slice computes the same total.
+    // The slot is written twice, to two regions: into the L2 that the row's
+    // slices share (they are placed on one XCD, above), and through to
+    // memory. Partners poll the first copy through the L2, a shorter round
+    // trip than to memory, and every eighth poll reads the second copy past
+    // the caches, so a placement that puts a partner on another XCD costs
+    // time, never a result. Each row's slots fill one 128-byte line of its
+    // own in each region, so the lines an XCD writes are written by no
+    // other XCD. Against one region at slot b, with cache-bypassing polls:
+    // N = 8, t = 8, d = 8192 chains 3.20-3.30 -> 2.95 us (4 slices), LL
+    // 4.34-4.40 -> 4.09 us (8 slices), FP4 t = 1 3.04-3.19 -> 2.86 us.
     __shared__ double xsum;
     if (lane < kWave) {
       const u32x2 tok = dispatch_token();
       char* wsb = (char*)a.ws;
-      const uint32_t wsbytes = row_blocks * 16;
+      const uint32_t region = prows * 128;  // bytes of one region
+      const uint32_t wsbytes = 2 * region;
       if (lane == 0) {
         const uint64_t tb = (uint64_t)__double_as_longlong(tot);
-        store16_through(wsb, wsbytes, blockIdx.x * 16, u32x4{(uint32_t)tb, (uint32_t)(tb >> 32), tok.x, tok.y});
+        const u32x4 slot = {(uint32_t)tb, (uint32_t)(tb >> 32), tok.x, tok.y};
+        const uint32_t own = (row * 8 + slice) * 16;
+        store16_l2(wsb, wsbytes, own, slot);
+        store16_through(wsb, wsbytes, region + own, slot);
       }
       double part = tot;
       uint32_t xbad = 0;
       if (lane < (1 << lg) && (uint32_t)lane != slice) {
-        const uint32_t off = ((row << lg) + (uint32_t)lane) * 16;
+        const uint32_t off = (row * 8 + (uint32_t)lane) * 16;
         u32x4 w = {0u, 0u, 0u, 0u};
         bool got = false;
         for (uint32_t i = 0; i < kExchangePolls; ++i) {
-          w = reread16(wsb, wsbytes, off);
+          w = (i & 7u) == 7u ? reread16(wsb, wsbytes, region + off) : reread16_l2(wsb, wsbytes, off);
           if ((w.z == tok.x) & (w.w == tok.y)) {
             got = true;
             break;

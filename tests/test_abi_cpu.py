@@ -324,12 +324,20 @@ def test_split_options_validated():
     assert call(**good(opts=arf._opts(split=2, workspace=spaced(11) + 16))) == arf.ARFUSE_ERR_INVALID_ARG
 
 
+def padded(t):
+    """Row positions of a split launch: t rounded up to a multiple of 8."""
+    return (t + 7) // 8 * 8
+
+
 @pytest.mark.parametrize("t,d,split,block,grid", [(8, 8192, 4, 256, 32), (8, 8192, 2, 512, 16),
-                                                 (1, 4096, 8, 64, 8), (64, 8192, 4, 256, 256)])
+                                                 (1, 4096, 8, 64, 64), (64, 8192, 4, 256, 256),
+                                                 (5, 8192, 4, 256, 32), (31, 4096, 8, 64, 256)])
 def test_query_launch_split(t, d, split, block, grid):
+    """A split launch runs split x (t rounded up to 8) workgroups, a slot each
+    (the padding row positions exit at once)."""
     info = arf.arfuse_query_launch(8, t, d, split=split)
     assert (info.grid, info.block, info.vpt, info.split) == (grid, block, 1, split)
-    assert info.workspace_bytes == 16 * t * split
+    assert info.workspace_bytes == 256 * padded(t)     # two 128-byte lines per row position
     plain = arf.arfuse_query_launch(8, t, d)
     assert (plain.split, plain.workspace_bytes, plain.grid) == (1, 0, t)
 
@@ -347,8 +355,9 @@ def test_auto_split_choice(shape, split):
     n, t, d, layout = shape
     info = arf.arfuse_query_launch(n, t, d, layout=layout, split=arf.ARFUSE_SPLIT_AUTO)
     assert info.split == split
-    assert info.workspace_bytes == (16 * t * split if split > 1 else 0)
-    assert info.grid == t * split
+    assert info.workspace_bytes == (256 * padded(t) if split > 1 else 0)
+    assert info.grid == (padded(t) * split if split > 1 else t)
+    assert info.grid <= arf.ARFUSE_MAX_SPLIT_BLOCKS or split == 1
     # the choice is what the explicit split would launch
     if split > 1:
         ex = arf.arfuse_query_launch(n, t, d, layout=layout, split=split)
@@ -416,4 +425,7 @@ def test_noalloc_refuses_a_workspace():
         rc = arf.lib.arfuse_rmsnorm_noalloc(arr, 4, spaced(8), spaced(9), 1e-5, spaced(10),
                                             spaced(11), None, None, t, 8192, None, ctypes.byref(o))
         assert rc == arf.ARFUSE_ERR_INVALID_ARG
-    assert arf.ARFUSE_NOALLOC_SLOTS == arf.ARFUSE_MAX_SPLIT_BLOCKS == 256
+    # the largest split call: 128 row positions (2 slices of 128 rows), 256 bytes each
+    assert arf.ARFUSE_NOALLOC_BYTES == arf.ARFUSE_MAX_SPLIT_BLOCKS // 2 * 256 == 32768
+    assert max(arf.arfuse_query_launch(8, t, 8192, split=s).workspace_bytes
+               for s in (2, 4, 8) for t in range(1, 256 // s + 1)) == arf.ARFUSE_NOALLOC_BYTES

@@ -130,3 +130,64 @@ def test_bench_record_is_compact_and_complete():
     assert set(line["decode"]) == names
     for want in ("C1_", "C2_", "C3_n4", "C3_n8", "_ll", "C5_n4_t1_", "C5_n4_t8_", "C5_n4_t64_"):
         assert any(want in x for x in names), want
+
+
+def _write_csv(path, header, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_profile_summaries_from_synthetic_rocprof_outputs(tmp_path):
+    """bench.py --summarize-profiles reads the CSV files the profile commands
+    write and produces every summary, with the byte counters scaled by the
+    copy calibration (synthetic counter values, no GPU)."""
+    out, dest = str(tmp_path / "prof"), str(tmp_path / "profiles")
+    stats_h = ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"]
+    pmc_h = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    row8 = "void arfuse_detail::row_kernel<8, 1, false, false, 1, 0>(arfuse_detail::RowArgs)"
+    mix = "void arfuse_detail::(anonymous namespace)::mix_kernel<1, false>(MixArgs)"
+    fp4 = "void arfuse_detail::row_kernel<4, 1, false, false, 2, 0>(arfuse_detail::RowArgs)"
+    _write_csv(os.path.join(out, "prof_trace", "prefill_kernel_stats.csv"), stats_h,
+               [[row8, 55, 117000, 116000, 119000, 99.0]])
+    for c, v in (("FETCH_SIZE", 295065.5), ("WRITE_SIZE", 131072.0)):
+        _write_csv(os.path.join(out, "pmc_prefill_%s" % c, "pmc_counter_collection.csv"), pmc_h,
+                   [[row8, c, v]] * 3)
+    for c, v in (("FETCH_SIZE", 524288.0), ("WRITE_SIZE", 1048576.0)):
+        _write_csv(os.path.join(out, "pmc_copy_%s" % c, "pmc_counter_collection.csv"), pmc_h,
+                   [["copy_kernel(...)", c, v]])
+    _write_csv(os.path.join(out, "prof_small", "small_kernel_stats.csv"), stats_h,
+               [[row8, 510, 16940, 14520, 22240, 50], [fp4, 510, 11330, 9400, 16360, 30],
+                [mix, 510, 16300, 15000, 18000, 20]])
+    for c, v in (("FETCH_SIZE", 37000.0), ("WRITE_SIZE", 16384.0)):
+        _write_csv(os.path.join(out, "pmc_small_%s" % c, "pmc_counter_collection.csv"), pmc_h,
+                   [[row8, c, v], [fp4, c, v / 2], [mix, c, v]])
+    kern = {lbl: "void arfuse_detail::%s(arfuse_detail::RowArgs)" % bench._counted_kernel(lbl)
+            for lbl in bench.DECODE_COUNTED}
+    _write_csv(os.path.join(out, "prof_counted", "decode_kernel_stats.csv"), stats_h,
+               [[k, 1600, 4000, 3000, 9000, 10] for k in kern.values()]
+               + [["floor_kernel(RowArgs)", 9600, 1300, 1000, 2000, 5]])
+    for key, counters in bench.DECODE_COUNTER_SETS.items():
+        rows = []
+        for k in kern.values():
+            for c in counters.split():
+                rows.append([k, c, 1400.0 * 18000 if "LEVEL" in c else 18000.0])
+        _write_csv(os.path.join(out, "pmc_counted_%s" % key, "pmc_counter_collection.csv"), pmc_h, rows)
+    bench.summarize_profiles(out, dest)
+    got = sorted(os.listdir(dest))
+    for f in ("row_kernel_prefill_n8_t4096_d8192_stats.md", "row_kernel_prefill_n8_t4096_d8192_traffic.json",
+              "row_kernel_prefill_t512_stats.md", "row_kernel_prefill_t512_traffic.json",
+              "row_kernel_decode_counters.md", "row_kernel_decode_counters.json"):
+        assert f in got, (f, got)
+    tr = json.load(open(os.path.join(dest, "row_kernel_prefill_n8_t4096_d8192_traffic.json")))
+    assert tr["copy_calibration"]["fetch_factor"] == 2.0
+    assert abs(tr["read_bytes_per_launch"] - 295065.5 * 1024 * 2) < 1
+    small = json.load(open(os.path.join(dest, "row_kernel_prefill_t512_traffic.json")))
+    assert set(small["workloads"]) == set(bench.SMALL_PREFILL_KERNELS)
+    dec = json.load(open(os.path.join(dest, "row_kernel_decode_counters.json")))
+    assert set(dec["chains"]) == set(bench.DECODE_COUNTED)
+    for rec in dec["chains"].values():
+        assert abs(rec["read_latency_cycles"] - 1400.0) < 1e-9

@@ -135,7 +135,8 @@ class Chain:
         self.n, self.t, self.d, self.k = n, t, d, k
         self.split = split
         # split rows: one workspace for every call of the chain, zeroed once
-        self.ws = (torch.zeros(16 * t * split, dtype=torch.uint8, device=DEV) if split > 1
+        self.ws = (torch.zeros(256 * ((t + 7) // 8 * 8), dtype=torch.uint8, device=DEV)
+                   if split > 1
                    else None)
         ci = si.make_call(n, t, d, seed=seed)
         self.ci = ci
@@ -271,7 +272,9 @@ def test_graph_chain_split_rows(n, t, d, k, per_call, ll, split):
         check_chain(ch, ref, what + " replay %d" % rep)
         ch.enqueue()
         torch.cuda.synchronize()
-    w = ch.ws.cpu().numpy().view(np.uint32).reshape(t * split, 4)
+    pt = (t + 7) // 8 * 8      # row positions; line r of each region holds row r's slots
+    w = ch.ws.cpu().numpy().view(np.uint32).reshape(2 * pt * 8, 4)
+    w = w[[reg * pt * 8 + r * 8 + s for reg in range(2) for r in range(t) for s in range(split)]]
     tok = w[:, 2].astype(np.uint64) | (w[:, 3].astype(np.uint64) << np.uint64(32))
     assert len(set(tok.tolist())) == 1 and int(tok[0]) & (1 << 32), \
         "every slot carries the last call's token"

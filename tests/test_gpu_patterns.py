@@ -304,7 +304,7 @@ def test_sentinel_triple_buffered_chain_in_graph(split):
     outs = torch.empty((k, t, d), dtype=torch.bfloat16, device=DEV)
     st = new_status()
     plane = t * d * 2
-    ws = torch.zeros(16 * t * split, dtype=torch.uint8, device=DEV) if split else None
+    ws = torch.zeros(256 * ((t + 7) // 8 * 8), dtype=torch.uint8, device=DEV) if split else None
 
     def enqueue():
         for c in range(k):

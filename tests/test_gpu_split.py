@@ -43,8 +43,20 @@ def read_status(st):
     return int(v[0]), int(v[1]), int(v[2]) | (int(v[3]) << 32)
 
 
+def padded(t):
+    """Row positions of a split launch: t rounded up to a multiple of 8."""
+    return (t + 7) // 8 * 8
+
+
 def workspace(t, split):
-    return torch.zeros(16 * t * split, dtype=torch.uint8, device=DEV)
+    return torch.zeros(256 * padded(t), dtype=torch.uint8, device=DEV)
+
+
+def active_slots(t, split):
+    """16-byte slot indices the real rows write: row r's slices fill line r
+    (8 slots) of each of the two regions of padded(t) lines."""
+    return ([r * 8 + s for r in range(t) for s in range(split)] +
+            [padded(t) * 8 + r * 8 + s for r in range(t) for s in range(split)])
 
 
 def assert_fp8_close(got, want, frac=1e-4):
@@ -199,9 +211,9 @@ def test_split_sentinel_pending_and_reset():
         assert np.all(sl.cpu().numpy().view(np.uint16) == pat)
 
 
-def slot_tokens(ws, nslots):
-    """The 64-bit tokens of the first `nslots` workspace slots."""
-    w = ws.cpu().numpy().view(np.uint32).reshape(-1, 4)[:nslots]
+def slot_tokens(ws, t, split):
+    """The 64-bit tokens of the slots of the real rows."""
+    w = ws.cpu().numpy().view(np.uint32).reshape(-1, 4)[active_slots(t, split)]
     return w[:, 2].astype(np.uint64) | (w[:, 3].astype(np.uint64) << np.uint64(32))
 
 
@@ -222,7 +234,7 @@ def test_split_tokens_over_calls_and_graph_replays():
     first = c.fetch()
     check(first, ref)
     seen = set()
-    tok = slot_tokens(ws, t * split)
+    tok = slot_tokens(ws, t, split)
     assert len(set(tok.tolist())) == 1 and int(tok[0]) & (1 << 32), tok
     seen.add(int(tok[0]))
 
@@ -244,12 +256,12 @@ def test_split_tokens_over_calls_and_graph_replays():
         assert read_status(st) == (0, 0, 0)
         for key in ("residual_out", "out", "codes", "scales"):
             assert np.array_equal(got[key], first[key]), key
-        tok = slot_tokens(ws, t * split)
+        tok = slot_tokens(ws, t, split)
         assert len(set(tok.tolist())) == 1 and int(tok[0]) not in seen, (rep, tok)
         seen.add(int(tok[0]))
         enqueue()
         torch.cuda.synchronize()
-        tok = slot_tokens(ws, t * split)
+        tok = slot_tokens(ws, t, split)
         assert len(set(tok.tolist())) == 1 and int(tok[0]) not in seen, (rep, tok)
         seen.add(int(tok[0]))
 
@@ -261,7 +273,7 @@ def test_split_ignores_stale_workspace_contents():
     cleared in between all give the oracle's outputs and a clean status."""
     n = 4
     shapes = [(3, 4096, 2), (8, 8192, 8), (5, 4096, 4), (8, 8192, 4), (1, 2048, 8), (3, 4096, 2)]
-    ws = torch.full((16 * 64,), 0xA5, dtype=torch.uint8, device=DEV)   # garbage
+    ws = torch.full((256 * 8,), 0xA5, dtype=torch.uint8, device=DEV)   # garbage
     st = new_status()
     for i, (t, d, split) in enumerate(shapes):
         ci = si.make_call(n, t, d, seed=260 + i)
@@ -278,7 +290,7 @@ def test_split_ignores_stale_workspace_contents():
         c.go(split=split, workspace=ws, status=st)
         check(c.fetch(), ref)
         assert read_status(st) == (0, 0, 0)
-        assert not torch.equal(saved[:16 * t * split], ws[:16 * t * split])
+        assert not torch.equal(saved[:256 * padded(t)], ws[:256 * padded(t)])
 
 
 # ARFUSE_SPLIT_AUTO: the library's choice for the shape, and the workspace
