@@ -190,6 +190,16 @@ def time_calls(fn, steps: int, warmup: int):
     return s.elapsed_time(e) / steps
 
 
+# graph replays per decode measurement (bench.py --decode-reps: fewer under a
+# profiler, which serializes and inflates every dispatch)
+DECODE_REPS = 200
+
+
+def set_decode_reps(reps: int) -> None:
+    global DECODE_REPS
+    DECODE_REPS = max(5, int(reps))
+
+
 def time_graph(g, reps: int):
     """p10/p50/p90 (µs) of `reps` replays of a captured graph, each bracketed
     by its own events."""
@@ -212,8 +222,9 @@ def time_graph(g, reps: int):
 # ------------------------------------------------------------ decode chains
 
 def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = False,
-                 out: bool = True, reps: int = 200, seed: int = 0, fp8: bool = False,
-                 sentinel: bool = False, fresh=None, split: int = 0, norm: bool = True):
+                 out: bool = True, reps: int = 0, seed: int = 0, fp8: bool = False,
+                 sentinel: bool = False, fresh=None, split: int = 0, norm: bool = True,
+                 block_threads: int = 0, vpt: int = 0):
     """µs per call of a k-call chain captured in one graph (call c reads call
     c-1's residual_out), and of the same-length graph of the empty kernel
     with the same launch (the per-node floor). `sentinel` reads the slots in
@@ -222,8 +233,9 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
     only) gives every call its own partial buffers, as a peer's push would,
     instead of re-reading one set that stays in the caches. `split` > 1
     divides every row among that many workgroups (sums of squares exchanged
-    through a zeroed workspace). `norm=False` is the all-reduce alone (no
-    gamma: residual_out is the only output)."""
+    through a workspace). `norm=False` is the all-reduce alone (no
+    gamma: residual_out is the only output). `block_threads` and `vpt`
+    override the launch shape (0: the library's choice)."""
     import numpy as np
     import torch
 
@@ -256,11 +268,12 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
     lay = (arf.ARFUSE_LAYOUT_LL if ll else
            arf.ARFUSE_LAYOUT_SENTINEL if sentinel else arf.ARFUSE_LAYOUT_PLAIN)
     # the split that runs (ARFUSE_SPLIT_AUTO: the library's choice for the shape)
-    info = arf.arfuse_query_launch(n, t, d, epi, layout=lay, split=split)
+    launch = dict(block_threads=block_threads, vpt=vpt)
+    info = arf.arfuse_query_launch(n, t, d, epi, layout=lay, split=split, **launch)
     eff = int(info.split)
     ws = (torch.zeros(int(info.workspace_bytes), dtype=torch.uint8, device=_dev())
           if info.workspace_bytes else None)
-    sx = dict(split=split, workspace=ws)
+    sx = dict(split=split, workspace=ws, **launch)
 
     def enqueue():
         for c in range(k):
@@ -270,7 +283,7 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
                 arf.arfuse_rmsnorm_ex(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales,
                                       layout=arf.ARFUSE_LAYOUT_LL, ll_flag=flags[c], max_polls=4,
                                       status=status, **sx)
-            elif sentinel or fp8 or split != 0 or not norm:
+            elif sentinel or fp8 or split != 0 or not norm or block_threads or vpt:
                 arf.arfuse_rmsnorm_ex(parts[c], rin, gamma, float(ci.eps), o, rout, codes, scales,
                                       t=t, d=d, layout=arf.ARFUSE_LAYOUT_SENTINEL if sentinel else 0,
                                       max_polls=4, status=status, reset=slots, fp8_out=f8,
@@ -280,7 +293,7 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
 
     def enqueue_floor():
         for _ in range(k):
-            arf.arfuse_launch_floor(n, t, d, epi, layout=lay, split=split)
+            arf.arfuse_launch_floor(n, t, d, epi, layout=lay, split=split, **launch)
 
     enqueue()
     torch.cuda.synchronize()
@@ -290,6 +303,7 @@ def decode_chain(n: int, t: int, d: int, k: int, ll: bool = False, fp4: bool = F
     gf = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gf):
         enqueue_floor()
+    reps = reps or DECODE_REPS
     chain = time_graph(g, reps)
     floor = time_graph(gf, reps)
     st = status.cpu().numpy().view(np.uint32)
@@ -473,8 +487,16 @@ DECODE_PROFILED = ("decode_n8_t8_d8192_chain160", "decode_n8_t8_d8192_chain160_l
 DECODE_SPLIT_PROFILED = ("decode_n8_t8_d8192_chain160_split4", "decode_n8_t8_d8192_chain160_ll_split4",
                          "decode_n8_t8_d8192_chain160_sentinel_split4", "fp4_n4_t1_d8192_x100_split8")
 
-# single-round prefill calls (512 rows: one workgroup per row, two per CU)
-SMALL_PREFILL_PROFILED = ("prefill_n8_t512_d8192", "fp4_n4_t512_d8192")
+# single-round prefill calls (512 rows: one workgroup per row, two per CU),
+# and the C4 call's byte mix without its arithmetic in the same launch shape
+SMALL_PREFILL_PROFILED = ("prefill_n8_t512_d8192", "fp4_n4_t512_d8192", "mix_9r2w_t512_d8192")
+
+# decode chains whose byte and latency counters are taken, one row-kernel
+# instance each: LL (fresh words per call) with whole and split rows at N = 8
+# and 4, and the plain N = 8 chain with whole and split rows
+DECODE_COUNTED = ("decode_n8_t8_d8192_chain160_ll", "decode_n8_t8_d8192_chain160_ll_split8",
+                  "decode_n4_t8_d8192_chain160_ll", "decode_n4_t8_d8192_chain160_ll_split8",
+                  "decode_n8_t8_d8192_chain160", "decode_n8_t8_d8192_chain160_split8")
 
 PROFILE_COMMANDS = {
     "trace": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
@@ -490,18 +512,34 @@ PROFILE_COMMANDS = {
                    "-d $OUT/prof_small -o small -- python3 $REPO/bench.py "
                    + " ".join("--only-extra " + x for x in SMALL_PREFILL_PROFILED),
     "pmc_small": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {C} --kernel-include-regex "
-                 "row_kernel -f csv -d $OUT/pmc_small_{C} -o pmc -- python3 $REPO/bench.py "
+                 "'row_kernel|mix_kernel' -f csv -d $OUT/pmc_small_{C} -o pmc -- python3 $REPO/bench.py "
                  + " ".join("--only-extra " + x for x in SMALL_PREFILL_PROFILED),
     "trace_decode": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
-                    "-d $OUT/prof_decode -o decode -- python3 $REPO/bench.py "
+                    "-d $OUT/prof_decode -o decode -- python3 $REPO/bench.py --decode-reps 20 "
                     + " ".join("--only-extra " + x for x in DECODE_PROFILED),
     "trace_decode_split": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
                           "-d $OUT/prof_decode_split -o decode -- python3 $REPO/bench.py "
+                          "--decode-reps 20 "
                           + " ".join("--only-extra " + x for x in DECODE_SPLIT_PROFILED),
+    "trace_counted": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -f csv "
+                     "-d $OUT/prof_counted -o decode -- python3 $REPO/bench.py --decode-reps 10 "
+                     + " ".join("--only-extra " + x for x in DECODE_COUNTED),
+    "pmc_counted": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {C} --kernel-include-regex "
+                   "'row_kernel|floor_kernel' -f csv -d $OUT/pmc_counted_{N} -o pmc -- python3 "
+                   "$REPO/bench.py --decode-reps 10 "
+                   + " ".join("--only-extra " + x for x in DECODE_COUNTED),
 }
+# the counter sets of the decode chains (one rocprofv3 run each): bytes fetched
+# and written past the L2, and the L2's outstanding read requests to the
+# fabric summed over cycles, whose ratio to the request count is the average
+# time a read spends past the L2 (Little's law)
+DECODE_COUNTER_SETS = {"fetch": "FETCH_SIZE", "write": "WRITE_SIZE",
+                       "lat": "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_LEVEL_sum"}
 
 
 def _bench_line(log_path):
+    if not os.path.exists(log_path):
+        return None
     with open(log_path) as f:
         for line in f:
             if line.startswith("{"):
@@ -515,10 +553,13 @@ def _counter(path, kname):
     return statistics.median(vals), len(vals)
 
 
-def summarize_profiles(outdir: str) -> None:
-    """Write profiles/row_kernel_<workload>_{stats.md,traffic.json} from the
-    rocprofv3 outputs of PROFILE_COMMANDS under `outdir` (their $OUT)."""
+def summarize_profiles(outdir: str, dest: str = PROFILES) -> None:
+    """Write profiles/row_kernel_<workload>_{stats.md,traffic.json} (into
+    `dest`) from the rocprofv3 outputs of PROFILE_COMMANDS under `outdir`
+    (their $OUT)."""
     import csv
+    global PROFILES
+    PROFILES = dest
     name = "prefill_n8_t4096_d8192"
     os.makedirs(PROFILES, exist_ok=True)
     line = _bench_line(os.path.join(outdir, "prof_trace.log"))
@@ -572,6 +613,8 @@ def summarize_profiles(outdir: str) -> None:
             summarize_decode_profile(outdir, which)
     if os.path.exists(os.path.join(outdir, "prof_small", "small_kernel_stats.csv")):
         summarize_small_prefill_profile(outdir, kf, kw)
+    if os.path.exists(os.path.join(outdir, "prof_counted", "decode_kernel_stats.csv")):
+        summarize_decode_counters(outdir, kf, kw)
 
 
 # the row-kernel instances of SMALL_PREFILL_PROFILED, as the tracer names them
@@ -579,6 +622,7 @@ SMALL_PREFILL_KERNELS = {
     "prefill_n8_t512_d8192": ("row_kernel<8, 1, false, false, 1, 0>", dict(n=8, t=512, d=8192)),
     "fp4_n4_t512_d8192": ("row_kernel<4, 1, false, false, 2, 0>",
                           dict(n=4, t=512, d=8192, out=False, fp4=True)),
+    "mix_9r2w_t512_d8192": ("mix_kernel<1, false>", dict(n=8, t=512, d=8192, mix=(9, 2))),
 }
 
 
@@ -612,8 +656,12 @@ def summarize_small_prefill_profile(outdir: str, kf: float, kw: float) -> None:
     for label, (kname, shape) in SMALL_PREFILL_KERNELS.items():
         fetch, nf = _counter(os.path.join(outdir, "pmc_small_FETCH_SIZE", "pmc_counter_collection.csv"), kname)
         write, nw = _counter(os.path.join(outdir, "pmc_small_WRITE_SIZE", "pmc_counter_collection.csv"), kname)
-        kw_shape = {k: v for k, v in shape.items() if k not in ("n", "t", "d")}
-        rd, wr = algorithmic_bytes(shape["n"], shape["t"], shape["d"], **kw_shape)
+        kw_shape = {k: v for k, v in shape.items() if k not in ("n", "t", "d", "mix")}
+        if "mix" in shape:      # n_in planes read, n_out written
+            rd, wr = (shape["mix"][0] * plane_bytes(shape["t"], shape["d"]),
+                      shape["mix"][1] * plane_bytes(shape["t"], shape["d"]))
+        else:
+            rd, wr = algorithmic_bytes(shape["n"], shape["t"], shape["d"], **kw_shape)
         rb, wb = fetch * 1024 * kf, write * 1024 * kw
         avg = [float(r["AverageNs"]) / 1e3 for r in rows if kname in r["Name"]]
         rec["workloads"][label] = {"kernel": kname, "dispatches": [nf, nw], "read_bytes": rb,
@@ -629,6 +677,10 @@ def summarize_small_prefill_profile(outdir: str, kf: float, kw: float) -> None:
         md += ["", "The same run's events (median window of back-to-back calls, tracer attached):", ""]
         for k, v in ex.items():
             md.append("- %s: %.2f µs per call" % (k, v["us_per_call"]))
+    md += ["", "`mix_kernel` is `arfuse_stream_mix` with 9 planes read and 2 written per row: "
+           "the C4 call's bytes in the C4 call's launch (512 workgroups of 1024 threads, "
+           "the same non-temporal loads and stores), without the arithmetic. Its time is the "
+           "ceiling of that launch shape."]
     with open(os.path.join(PROFILES, "row_kernel_prefill_t512_stats.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     with open(os.path.join(PROFILES, "row_kernel_prefill_t512_traffic.json"), "w") as f:
@@ -676,6 +728,74 @@ def summarize_decode_profile(outdir: str, which: str = "decode") -> None:
         f.write("\n".join(md) + "\n")
 
 
+# the row-kernel instance of each counted decode chain, as the tracer names it
+def _counted_shape(label):
+    n = int(label.split("_n")[1].split("_")[0])
+    return dict(n=n, t=8, d=8192, ll="_ll" in label,
+                split=8 if "split8" in label else 1)
+
+
+def _counted_kernel(label):
+    sh = _counted_shape(label)
+    return "row_kernel<%d, 1, %s, false, 1, %d>" % (sh["n"], "true" if sh["ll"] else "false",
+                                                    1 if sh["split"] > 1 else 0)
+
+
+def summarize_decode_counters(outdir: str, kf: float, kw: float) -> None:
+    """profiles/row_kernel_decode_counters.md: per decode chain, the kernel's
+    traced duration, bytes fetched and written past the L2 (scaled by the
+    copy calibration), and the average time a fabric read request spends
+    outstanding (TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ, in L2 clock cycles)."""
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(outdir, "prof_counted", "decode_kernel_stats.csv"))))
+
+    def med(which, kname, counter):
+        path = os.path.join(outdir, "pmc_counted_%s" % which, "pmc_counter_collection.csv")
+        v = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+             if kname in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        return statistics.median(v) if v else float("nan")
+
+    md = ["# row_kernel, decode chains: bytes past the L2 and fabric read latency", "",
+          "Commands (`$REPO` is the repository root, `$OUT` the output directory):", "",
+          "    " + PROFILE_COMMANDS["trace_counted"], ""]
+    for key, counters in DECODE_COUNTER_SETS.items():
+        md.append("    " + PROFILE_COMMANDS["pmc_counted"].format(C=counters, N=key))
+    md += ["", "Kernel source sha256[:16]: `%s`" % source_digest(), "",
+           "Each chain is one row-kernel instance, captured in a graph of 160 calls "
+           "(t = 8, d = 8192) and replayed; LL chains give every call its own words and flag "
+           "(fresh from HBM), plain chains re-read one partial set. Under the profiler every "
+           "dispatch runs alone, so durations are longer than in the untraced graphs and the "
+           "caches see only one call at a time. Byte counters are medians per dispatch, scaled "
+           "by the copy calibration (fetch x%.3f, write x%.3f). Latency: median over dispatches "
+           "of the summed outstanding fabric read requests per cycle divided by the number of "
+           "requests." % (kf, kw), "",
+           "| chain | kernel | traced µs | algorithmic read / write bytes | fetched bytes | "
+           "written bytes | fabric read latency (cycles) |", "|---|---|---|---|---|---|---|"]
+    rec = {}
+    for label in DECODE_COUNTED:
+        sh = _counted_shape(label)
+        kname = _counted_kernel(label)
+        rd, wr = algorithmic_bytes(sh["n"], sh["t"], sh["d"], ll=sh["ll"])
+        avg = [float(r["AverageNs"]) / 1e3 for r in rows if kname in r["Name"]]
+        fb = med("fetch", kname, "FETCH_SIZE") * 1024 * kf
+        wb = med("write", kname, "WRITE_SIZE") * 1024 * kw
+        lat = med("lat", kname, "TCC_EA0_RDREQ_LEVEL_sum") / med("lat", kname, "TCC_EA0_RDREQ_sum")
+        rec[label] = dict(kernel=kname, traced_us=avg[0] if avg else None, read=rd, write=wr,
+                          fetched=fb, written=wb, read_latency_cycles=lat)
+        md.append("| %s | `%s` | %s | %d / %d | %.0f | %.0f | %.0f |" % (
+            label, kname, "%.2f" % avg[0] if avg else "?", rd, wr, fb, wb, lat))
+    fl = [r for r in rows if "floor_kernel" in r["Name"]]
+    if fl:
+        md += ["", "The empty kernel of the same launches averages %.2f µs under this tracer." %
+               (float(fl[0]["AverageNs"]) / 1e3)]
+    with open(os.path.join(PROFILES, "row_kernel_decode_counters.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    with open(os.path.join(PROFILES, "row_kernel_decode_counters.json"), "w") as f:
+        json.dump(dict(source_sha256_16=source_digest(), copy_factors=dict(fetch=kf, write=kw),
+                       chains=rec), f, indent=1)
+        f.write("\n")
+
+
 # ------------------------------------------------------------ extras
 
 def extra_table():
@@ -683,6 +803,10 @@ def extra_table():
     t = {"stream_copy_1GiB": stream_copy_gbps,
          "prefill_n8_t512_d8192": lambda: prefill_gbps(8, 512, 8192, 100, 10),
          "fp4_n4_t512_d8192": lambda: prefill_gbps(4, 512, 8192, 100, 10, fp4=True, out=False),
+         # the same byte mixes without the arithmetic, in the calls' launch shapes
+         "mix_9r2w_t512_d8192": lambda: mix_gbps(9, 2, 512, 8192, 100, 10),
+         "mix_5r1w_t512_d8192": lambda: mix_gbps(5, 1, 512, 8192, 100, 10),
+         "mix_9r2w_t4096_d8192": lambda: mix_gbps(9, 2, 4096, 8192, 30, 5),
          # wide rows (the kernel's chunk pipeline), same bytes as the timed workload
          "prefill_n8_t1024_d32768": lambda: prefill_gbps(8, 1024, 32768, 30, 5),
          "prefill_n8_t512_d65536": lambda: prefill_gbps(8, 512, 65536, 30, 5)}
@@ -714,6 +838,7 @@ def extra_table():
             (8, 8, 8192, 160, "ll_split4", False, "decode_n8_t8_d8192_chain160_ll_split4"),
             (8, 8, 8192, 160, "sentinel_split4", False, "decode_n8_t8_d8192_chain160_sentinel_split4"),
             (8, 8, 8192, 160, "ll_split8", False, "decode_n8_t8_d8192_chain160_ll_split8"),
+            (4, 8, 8192, 160, "ll_split8", False, "decode_n4_t8_d8192_chain160_ll_split8"),
             (8, 8, 8192, 160, "fresh_split4", False, "decode_n8_t8_d8192_chain160_fresh_split4"),
             (8, 8, 8192, 160, "sentinel_fresh_split4", False,
              "decode_n8_t8_d8192_chain160_sentinel_fresh_split4"),
@@ -892,6 +1017,8 @@ def main(argv=None):
     ap.add_argument("--extras-out", default=os.path.join("gpurun_out", "bench_extras.json"),
                     help="JSON file for the full records of every secondary measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-reps", type=int, default=200,
+                    help="graph replays per decode measurement")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the streaming-copy reference (counter calibration)")
     ap.add_argument("--only-extra", action="append", metavar="LABEL",
@@ -899,9 +1026,12 @@ def main(argv=None):
                          "print them as one JSON object; repeatable")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 outputs under DIR, then exit")
+    ap.add_argument("--profiles-dest", default=PROFILES,
+                    help="directory the --summarize-profiles summaries are written to")
     args = ap.parse_args(argv)
+    set_decode_reps(args.decode_reps)
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles)
+        summarize_profiles(args.summarize_profiles, args.profiles_dest)
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
