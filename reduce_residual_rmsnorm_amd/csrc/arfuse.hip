@@ -312,9 +312,9 @@ int auto_split_log2(int n, int64_t t, int64_t d, bool ll, bool norm) {
 }
 
 // Split rows launch their slices at row positions 0..prows-1, prows being t
-// rounded up to a multiple of 8, so that slice b / prows of row b % prows
-// shares b mod 8 (its XCD) with the row's other slices; rows past t are
-// padding. With t * split <= ARFUSE_MAX_SPLIT_BLOCKS and split <= 8, the
+// rounded up to a multiple of 8, so that every slice of a row can take the
+// same b mod 8 (its XCD; the kernel maps workgroup b to its row and slice
+// with shifts and masks); rows past t are padding. With t * split <= ARFUSE_MAX_SPLIT_BLOCKS and split <= 8, the
 // padded launch prows * split fits the same cap (256 / split is a multiple of
 // 8).
 int64_t split_rows(int64_t t, int lg) { return lg ? (t + 7) / 8 * 8 : t; }

@@ -649,12 +649,17 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
       return;
     }
   }
-  // this workgroup's columns: the whole row, or one slice of a split row
-  // (row b mod prows, so every slice of a row has the same b mod 8: the
-  // workgroups of a launch go to the XCDs in turn, b mod 8, and a row's
-  // slices then share an L2 for their exchange)
-  const uint32_t row = SPLIT ? blockIdx.x % prows : blockIdx.x;
-  const uint32_t slice = SPLIT ? blockIdx.x / prows : 0u;
+  // this workgroup's columns: the whole row, or one slice of a split row.
+  // The workgroups of a launch go to the XCDs in turn (b mod 8), so with
+  // j = b / 8 the index of b among its XCD's workgroups, b takes slice
+  // j mod S of row 8 (j / S) + b mod 8: a row's slices share an XCD, and
+  // its L2 for their exchange, and are consecutive there, dispatched
+  // together. Shifts and masks (prows is a multiple of 8), where a modulo by
+  // the runtime prows was a scalar division sequence before the first load:
+  // 0.025-0.045 us per decode call with t > 8.
+  const uint32_t bj = blockIdx.x >> 3;
+  const uint32_t row = SPLIT ? ((bj >> lg) << 3) | (blockIdx.x & 7u) : blockIdx.x;
+  const uint32_t slice = SPLIT ? bj & ((1u << lg) - 1u) : 0u;
   if constexpr (SPLIT) {
     if (row >= a.rows) return;  // padding row position
   }
@@ -822,13 +827,17 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
       }
     }
   };
-  // chunk k's share of the sum of squares; without a norm, its residual_out.
-  // A normalizing call stores residual_out next to y, in the output loop, so
-  // the row's two output streams reach HBM together, after its reads, rather
-  // than one in the middle of them. Prefill N=8 d=8192: t=4096 1-1.5% faster,
-  // t=512 1%, d=32768 2.5-3.5%; decode calls within +-0.1 us either way.
+  // chunk k's share of the sum of squares; without a norm, or in a split
+  // row, its residual_out.
+  // A whole row that normalizes stores residual_out next to y, in the output
+  // loop, so the row's two output streams reach HBM together, after its
+  // reads, rather than one in the middle of them. Prefill N=8 d=8192: t=4096
+  // 1-1.5% faster, t=512 1%, d=32768 2.5-3.5%; whole-row decode calls within
+  // +-0.06 us either way. A split row stores it here, before the exchange,
+  // whose wait the stores then overlap: 160-call chains 0.03-0.12 us faster
+  // (FP4 t=64 3.24 -> 3.17 us, N=8 t=8 3.01 -> 2.94, LL N=8 4.08 -> 4.04).
   auto after_sum = [&](int k) {
-    if constexpr (!NORM) store_residual(k);
+    if constexpr (!NORM || SPLIT) store_residual(k);
     if constexpr (NORM) {
       // h is fp32, so h * h is exact in fp64 and the fused multiply-add
       // rounds exactly as the separate product and sum would
@@ -999,7 +1008,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
                          g[k][1].x, g[k][1].y, g[k][1].z, g[k][1].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = (h[k][e] * inv) * gg[e];
-    store_residual(k);
+    if constexpr (!SPLIT) store_residual(k);
     if constexpr (OUT) {
       const u32x4 yb = narrow8(y);
       if constexpr (LL) {
