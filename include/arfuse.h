@@ -375,9 +375,11 @@ int arfuse_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
  * of the n_in input planes (device, [t][d] 16-bit elements, 16-byte aligned)
  * and writes the XOR of them to row r of each of the n_out output planes
  * (device, [t][d], 16-byte aligned, overlapping no other plane). One
- * workgroup per row with the block, vectors per thread, load policy and
- * output store policy the fused call uses for that t and d; every load of a
- * row is issued before the first store. The time of a call is the bandwidth
+ * workgroup per row with the block and vectors per thread the fused call
+ * uses for that t and d, non-temporal loads, and the fused call's
+ * write-through stores where its rows take several rounds of workgroups,
+ * else non-temporal stores; every load of a row is issued before the first
+ * store. The time of a call is the bandwidth
  * ceiling of the fused call's memory traffic at that shape (Deep Dive §6.1,
  * §6.4: the fused kernel's cost is its HBM transactions). n_in in [1, 9],
  * n_out in [1, 3]; d % 16 == 0, d <= ARFUSE_MAX_D.

@@ -91,10 +91,16 @@ __global__ __launch_bounds__(256) void quant_ll_kernel(const f32x4* y, int64_t n
 }
 
 // The fused call's byte mix without its arithmetic: one workgroup per row,
-// the row kernel's lane geometry, vectors per thread, non-temporal loads and
-// output store policy; row r of every output plane receives the XOR of row r
-// of the input planes. Every load of the row is issued before the first use,
-// as in a row-kernel instance that holds its whole row.
+// the row kernel's lane geometry and vectors per thread, non-temporal loads;
+// the streaming instances' write-through stores where the fused call takes
+// them (several rounds of workgroups), else non-temporal stores. Row r of
+// every output plane receives the XOR of row r of the input planes. Every
+// load of the row is issued before the first use, as in a row-kernel
+// instance that holds its whole row. (With the default-policy stores and
+// residual loads of the fused call's one-round instances, this kernel, which
+// stores each vector as soon as its own loads land, is slower: t=512 N=8
+// 18.7 us against 16.4; the fused call's rows store only after their row's
+// reduction.)
 constexpr int kMixMaxIn = ARFUSE_MAX_PARTIALS + 1;
 constexpr int kMixMaxOut = 3;
 struct MixArgs {
@@ -134,7 +140,8 @@ __global__ __launch_bounds__(kMaxBlock) void mix_kernel(MixArgs a) {
     if (ok[k]) {
 #pragma unroll
       for (int o = 0; o < kMixMaxOut; ++o)
-        if (o < a.n_out) out_store<STREAM>((char*)a.out[o] + rb, off[k], x);
+        if (o < a.n_out)
+          out_store<STREAM ? kStoreThrough : kStoreNT>((char*)a.out[o] + rb, off[k], x);
     }
   }
 }
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(256) void round_fp4_kernel(const f32x2* x, int64_t 
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* src, u32x4* dst, int64_t n) {
   const int64_t b = (int64_t)blockIdx.x * blockDim.x;
   const int64_t i = b + threadIdx.x;
-  if (i < n) out_store<true>((char*)(dst + b), threadIdx.x * 16u, load16<true>(src + i));
+  if (i < n) out_store<kStoreThrough>((char*)(dst + b), threadIdx.x * 16u, load16<true>(src + i));
 }
 
 // ------------------------------------------------------------ dispatch

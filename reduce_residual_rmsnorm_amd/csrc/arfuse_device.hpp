@@ -490,7 +490,7 @@ __device__ __forceinline__ u32x2 load8(const u32x2* p) {
     return *p;
 }
 
-__device__ __forceinline__ void store8(u32x2* p, u32x2 v) { __builtin_nontemporal_store(v, p); }
+
 
 // FP4 of a 4-element group in the LL geometry: lanes 4m..4m+3 hold one
 // 16-element block (two lane swaps give its max); 4 codes = 16 bits.
@@ -546,21 +546,27 @@ __device__ __forceinline__ T* at_w(char* base, uint32_t off) {
   return reinterpret_cast<T*>(base + off);
 }
 
-// A row output store at byte `off` from the row's base `base` (uniform).
-// Non-temporal by default: at decode the next call reads residual_out right
-// away. STREAM instances (chosen by the host when a call's rows take several
-// rounds of workgroups: prefill) store with device scope (sc1) through a
-// buffer descriptor of the row, which writes through to memory instead of
-// leaving the lines to the L2. Prefill N=8 t=4096 d=8192 121.0 -> 117.2 us,
-// the all-reduce alone 114.3 -> 109.1, d=32768 t=1024 131 -> 122 us, on the
-// same box. A single round of workgroups (t=512) gains nothing, and decode
-// loses 0.25-0.45 us per call with these stores (the next call's reads of
-// residual_out miss), so those keep the non-temporal store. The choice is a
+// Row output store policies. STREAM instances (chosen by the host when a
+// call's rows take several rounds of workgroups: prefill) store with device
+// scope (sc1) through a buffer descriptor of the row, which writes through
+// to memory instead of leaving the lines to the L2: prefill N=8 t=4096
+// d=8192 121.0 -> 117.2 us, the all-reduce alone 114.3 -> 109.1, d=32768
+// t=1024 131 -> 122 us, on the same box; decode loses 0.25-0.45 us per call
+// with these stores (the next call's reads of residual_out miss). Whole rows
+// in one round of workgroups or less (decode, t=512) store with the default
+// policy, into the L2, which writes the lines back as the kernel ends, and
+// load the residual with the default policy too: t=512 N=8 16.9 -> 15.9-16.0
+// us against non-temporal stores and loads, whole-row decode chains within
+// 0.005 us. Split rows keep non-temporal stores and residual loads, 0.005-
+// 0.014 us per decode call faster than the default policy. The choice is a
 // template parameter: as a run-time branch it cost every decode call 0.05 us.
+constexpr int kStoreNT = 0;       // non-temporal
+constexpr int kStoreL2 = 1;       // default policy
+constexpr int kStoreThrough = 2;  // device scope (sc1), written through
 constexpr int kStreamPolicy = 0x10;  // sc1
-template <bool STREAM, typename T>
+template <int POL, typename T>
 __device__ __forceinline__ void out_store(char* base, uint32_t off, T v) {
-  if constexpr (STREAM) {
+  if constexpr (POL == kStoreThrough) {
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, kBufferWord3);
     if constexpr (sizeof(T) == 16)
@@ -569,8 +575,10 @@ __device__ __forceinline__ void out_store(char* base, uint32_t off, T v) {
       __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kStreamPolicy);
     else
       __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kStreamPolicy);
-  } else {
+  } else if constexpr (POL == kStoreNT) {
     __builtin_nontemporal_store(v, at_w<T>(base, off));
+  } else {
+    *at_w<T>(base, off) = v;
   }
 }
 
@@ -599,6 +607,10 @@ template <int N, int VPT, bool LL, bool SENT, int EPI, int KIND>
 __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   constexpr bool SPLIT = KIND == kRowSplit;
   constexpr bool STREAM = KIND == kRowStream;
+  // output store policy, and whether the residual is loaded non-temporally
+  // (see out_store)
+  constexpr int SPOL = STREAM ? kStoreThrough : SPLIT ? kStoreNT : kStoreL2;
+  constexpr bool RES_NT = KIND != kRowWhole;
   constexpr bool NORM = EPI != 0;
   constexpr bool OUT = (EPI & ARFUSE_EPI_BF16) != 0;
   constexpr bool FP4 = (EPI & ARFUSE_EPI_FP4) != 0;
@@ -738,11 +750,11 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     rres[k] = u32x4{0, 0, 0, 0};
     if (has_res) {
       if constexpr (LL) {
-        const u32x2 r0 = load8<true>(at<u32x2>(rrow, eo[k][0] * 2));
-        const u32x2 r1 = load8<true>(at<u32x2>(rrow, eo[k][1] * 2));
+        const u32x2 r0 = load8<RES_NT>(at<u32x2>(rrow, eo[k][0] * 2));
+        const u32x2 r1 = load8<RES_NT>(at<u32x2>(rrow, eo[k][1] * 2));
         rres[k] = u32x4{r0.x, r0.y, r1.x, r1.y};
       } else {
-        rres[k] = load16<true>(at<u32x4>(rrow, eo[k][0] * 2));
+        rres[k] = load16<RES_NT>(at<u32x4>(rrow, eo[k][0] * 2));
       }
     }
     if constexpr (G_EARLY) load_gamma(k);
@@ -820,10 +832,10 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     if (has_rout) {
       const u32x4 hb = narrow8(h[k]);
       if constexpr (LL) {
-        if (ok[k][0]) store8(at_w<u32x2>(orow, eo[k][0] * 2), u32x2{hb.x, hb.y});
-        if (ok[k][1]) store8(at_w<u32x2>(orow, eo[k][1] * 2), u32x2{hb.z, hb.w});
+        if (ok[k][0]) out_store<SPOL>(orow, eo[k][0] * 2, u32x2{hb.x, hb.y});
+        if (ok[k][1]) out_store<SPOL>(orow, eo[k][1] * 2, u32x2{hb.z, hb.w});
       } else if (ok[k][0]) {
-        out_store<STREAM>(orow, eo[k][0] * 2, hb);
+        out_store<SPOL>(orow, eo[k][0] * 2, hb);
       }
     }
   };
@@ -1012,19 +1024,19 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     if constexpr (OUT) {
       const u32x4 yb = narrow8(y);
       if constexpr (LL) {
-        if (ok[k][0]) store8(at_w<u32x2>(yrow, eo[k][0] * 2), u32x2{yb.x, yb.y});
-        if (ok[k][1]) store8(at_w<u32x2>(yrow, eo[k][1] * 2), u32x2{yb.z, yb.w});
+        if (ok[k][0]) out_store<SPOL>(yrow, eo[k][0] * 2, u32x2{yb.x, yb.y});
+        if (ok[k][1]) out_store<SPOL>(yrow, eo[k][1] * 2, u32x2{yb.z, yb.w});
       } else if (ok[k][0]) {
-        out_store<STREAM>(yrow, eo[k][0] * 2, yb);
+        out_store<SPOL>(yrow, eo[k][0] * 2, yb);
       }
     }
     if constexpr (FP8) {
       const uint32_t q[2] = {fp8_quad(y, a.fp8_inv_scale), fp8_quad(y + 4, a.fp8_inv_scale)};
       if constexpr (LL) {
-        if (ok[k][0]) __builtin_nontemporal_store(q[0], at_w<uint32_t>(frow, eo[k][0]));
-        if (ok[k][1]) __builtin_nontemporal_store(q[1], at_w<uint32_t>(frow, eo[k][1]));
+        if (ok[k][0]) out_store<SPOL>(frow, eo[k][0], q[0]);
+        if (ok[k][1]) out_store<SPOL>(frow, eo[k][1], q[1]);
       } else if (ok[k][0]) {
-        out_store<STREAM>(frow, eo[k][0], u32x2{q[0], q[1]});
+        out_store<SPOL>(frow, eo[k][0], u32x2{q[0], q[1]});
       }
     }
     if constexpr (FP4) {
@@ -1042,7 +1054,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
         uint32_t c8, sc;
         fp4_pair(y, c8, sc);
         if (ok[k][0]) {
-          out_store<STREAM>(crow, eo[k][0] / 2, c8);
+          out_store<SPOL>(crow, eo[k][0] / 2, c8);
           if ((eo[k][0] & 15) == 0) *at_w<uint8_t>(srow, eo[k][0] / 16) = (uint8_t)sc;
         }
       }
