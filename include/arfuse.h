@@ -221,8 +221,11 @@ typedef struct {
                            the choice for ARFUSE_SPLIT_AUTO) */
   int32_t stream_stores; /* 1: the outputs are written through to memory
                            (calls whose rows take several rounds of
-                           workgroups: t * vpt >= 1024, not LL); 0: non-
-                           temporal stores that may stay in the caches */
+                           workgroups: t * vpt >= 1024, not LL); 0: they
+                           stay in the caches for the next call (whole
+                           rows: default-policy stores, written back at
+                           the end of the kernel; split rows: non-temporal
+                           stores) */
   int64_t workspace_bytes; /* bytes of opts->workspace a split call needs */
 } arfuse_launch_info;
 
