@@ -167,7 +167,7 @@ typedef struct {
                                  workgroups on different CUs, which exchange
                                  the row's sum of squares through workspace
                                  (decode shapes, where a row is bound by one
-                                 CU's issue rate). Needs workspace,
+                                 CU's fetch). Needs workspace,
                                  d % (16 * split) == 0 and
                                  t * split <= ARFUSE_MAX_SPLIT_BLOCKS; a
                                  slice of more than 16,384 elements (or a vpt
@@ -278,11 +278,11 @@ int arfuse_rmsnorm(const void* const* partials, int n_partials, const void* resi
  *
  * opts->split > 1 divides every row's columns between that many workgroups
  * (on different CUs of one XCD where the workgroups of a launch are placed on
- * the XCDs in turn: a row's slices are launched 8k workgroups apart). Each
- * computes its columns' share of the sum of squares, writes it with its
- * dispatch's token to its slot of opts->workspace and waits (bounded) for the
- * row's other slots to carry the same token; the shares
- * are added in slice order, so the result is deterministic (it may differ in
+ * the XCDs in turn: a row's slices are workgroups 8 apart). Each computes its
+ * columns' share of the sum of squares, writes it with its dispatch's token
+ * to its slot of opts->workspace and waits (bounded) for the row's other
+ * slots to carry the same token; the shares are added in slice order, so the
+ * result is deterministic (it may differ in
  * the last bits from the unsplit call, whose sum runs in another order).
  * residual_out, the FP4 and the FP8 outputs are produced per slice exactly as
  * without the split. The operation is unchanged (the mean square is over the

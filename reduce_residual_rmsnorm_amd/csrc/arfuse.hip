@@ -302,7 +302,7 @@ int64_t work_per_simd(int64_t vecs) {
 // partials per workgroup, within the split limits; kept only where it removes
 // at least three waves' work per SIMD or the unsplit workgroup would read
 // 128 KiB or more. Measured on MI355X decode chains: the exchange costs about
-// 1 us, and a CU fetching data the caches do not hold reads a few tens of
+// 0.75 us, and a CU fetching data the caches do not hold reads a few tens of
 // GB/s, so a row's bytes are best spread thin once they are many.
 // The all-reduce alone (no norm) needs no exchange, so it splits whenever
 // the row reads 32 KiB or more.
@@ -321,9 +321,9 @@ int auto_split_log2(int n, int64_t t, int64_t d, bool ll, bool norm) {
 // Split rows launch their slices at row positions 0..prows-1, prows being t
 // rounded up to a multiple of 8, so that every slice of a row can take the
 // same b mod 8 (its XCD; the kernel maps workgroup b to its row and slice
-// with shifts and masks); rows past t are padding. With t * split <= ARFUSE_MAX_SPLIT_BLOCKS and split <= 8, the
-// padded launch prows * split fits the same cap (256 / split is a multiple of
-// 8).
+// with shifts and masks); rows past t are padding. With
+// t * split <= ARFUSE_MAX_SPLIT_BLOCKS and split <= 8, the padded launch
+// prows * split fits the same cap (256 / split is a multiple of 8).
 int64_t split_rows(int64_t t, int lg) { return lg ? (t + 7) / 8 * 8 : t; }
 
 // Bytes of a split call's exchange slots: two regions of one 128-byte line

@@ -46,8 +46,9 @@ struct RowArgs {
   uint32_t reset_bpp;   // reset blocks per plane (plane_vecs / block, rounded up)
   // split rows: the launch has prows = rows rounded up to a multiple of 8
   // row positions per slice; workgroup b < prows << split_log2 takes column
-  // slice b / prows of row b % prows (rows past `rows` are padding and exit),
-  // so a row's workgroups share b mod 8, i.e. one XCD. They exchange their
+  // slice j mod S of row 8 (j / S) + b mod 8, with j = b / 8 and S the
+  // split (rows past `rows` are padding and exit), so a row's workgroups
+  // share b mod 8, i.e. one XCD. They exchange their
   // sums of squares through ws: two regions of prows 128-byte lines, line r
   // holding row r's slots (slot = {fp64 share, 64-bit token of the
   // dispatch}), the first written and read through the L2, the second
@@ -489,8 +490,6 @@ __device__ __forceinline__ u32x2 load8(const u32x2* p) {
   else
     return *p;
 }
-
-
 
 // FP4 of a 4-element group in the LL geometry: lanes 4m..4m+3 hold one
 // 16-element block (two lane swaps give its max); 4 codes = 16 bits.
