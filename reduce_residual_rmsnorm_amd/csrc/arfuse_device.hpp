@@ -617,17 +617,20 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   constexpr int D = pipeline_depth<N, VPT, LL>();
   constexpr bool ALL_AT_ONCE = D == VPT;
   constexpr int W = LL ? 2 : 1;  // 16-byte loads per partial per chunk
-  // gamma, when the whole row's loads fit at once: a split row's slice loads
-  // it with its partials (plain, LL) or right after the arrival check
-  // (sentinel, so the re-poll path's registers stay free). A whole row loads
-  // it after its rank sum: gamma is not needed before the row's norm, and
-  // left out of the first loads it does not share the one CU's fetch with
-  // the partials (decode chains 0.03-0.1 us faster; split rows, whose
-  // slices fetch little, measured 0.05-0.17 us slower that way). Wide rows
-  // load it per chunk in the output loop.
-  constexpr bool G_EARLY = NORM && ALL_AT_ONCE && SPLIT && !SENT;
+  // gamma, when the whole row's loads fit at once: a split row's slice and a
+  // streaming (several-round) row load it with their partials, except in
+  // the sentinel layout: there a split slice loads it right after the
+  // arrival check, so the re-poll path's registers stay free, and a
+  // streaming row after its rank sum. A whole row in one round loads it
+  // after its rank sum: gamma is not needed before the row's norm, and left
+  // out of the first loads it does not share the one CU's fetch with the
+  // partials (decode chains 0.03-0.1 us faster, t=512 0.45 us faster; split
+  // rows, whose slices fetch little, measured 0.05-0.17 us slower that way,
+  // and the timed prefill 1.2% slower). Wide rows load it per chunk in the
+  // output loop.
+  constexpr bool G_EARLY = NORM && ALL_AT_ONCE && (SPLIT || STREAM) && !SENT;
   constexpr bool G_AFTER_ARRIVAL = NORM && ALL_AT_ONCE && SPLIT && SENT;
-  constexpr bool G_AFTER_SUM = NORM && ALL_AT_ONCE && !SPLIT;
+  constexpr bool G_AFTER_SUM = NORM && ALL_AT_ONCE && !SPLIT && !G_EARLY;
   const int lane = threadIdx.x;
   const int nthr = blockDim.x;
   if constexpr (SPLIT) {
