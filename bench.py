@@ -155,6 +155,8 @@ class PrefillSets:
             f8 = torch.empty((t, d), dtype=torch.uint8, device=_dev()) if fp8 else None
             slots = [torch.empty_like(res0) for _ in parts] if reset else None
             self.sets.append((parts, res, gamma, o, ro, codes, scales, f8, slots))
+        # the sentinel layout can wait, so its calls take a status word
+        self.status = torch.zeros(4, dtype=torch.int32, device=_dev()) if reset else None
 
     def call(self, i: int):
         import reduce_residual_rmsnorm_amd as arf
@@ -165,7 +167,7 @@ class PrefillSets:
         arf.arfuse_rmsnorm_ex(parts, res, gamma, float(self.ci.eps), o, ro, codes, scales,
                               t=self.ci.t, d=self.ci.d,
                               layout=arf.ARFUSE_LAYOUT_SENTINEL if self.reset else 0,
-                              reset=slots, fp8_out=f8, fp8_inv_scale=4.0)
+                              reset=slots, fp8_out=f8, fp8_inv_scale=4.0, status=self.status)
 
 
 def n_sets_for(call_bytes: int) -> int:
