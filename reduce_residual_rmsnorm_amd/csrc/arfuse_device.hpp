@@ -284,8 +284,12 @@ __device__ __forceinline__ bool ll_ok(u32x4 w, uint64_t flag) {
 // reader sees either the old word or all of the new one.
 __device__ __forceinline__ void store16_through(char* base, uint32_t bytes, uint32_t off, u32x4 v);
 
-// Re-read through the L2 (sc0: past the L1 only), for a partner workgroup on
-// the same XCD, which shares that L2.
+// The re-read of a split row's exchange slot in the region its partners on
+// the same XCD find in their L2. The compiler issues it exactly as reread16
+// (a volatile buffer load gets sc0 sc1); its own policy immediate (sc0 and
+// volatile) only keeps the two polls of the exchange loop two instructions
+// the compiler does not merge: merged, split chains moved by -0.01 to
+// +0.025 us per call.
 constexpr int kRereadL2Policy = (int)0x80000001u;
 __device__ __forceinline__ u32x4 reread16_l2(const char* row, uint32_t row_bytes, uint32_t off) {
   const __amdgpu_buffer_rsrc_t r =
@@ -293,8 +297,9 @@ __device__ __forceinline__ u32x4 reread16_l2(const char* row, uint32_t row_bytes
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kRereadL2Policy);
 }
 
-// Store of a 16-byte word for partners on the same XCD (sc0: through the L1
-// into the shared L2).
+// Store of a 16-byte word for partners on the same XCD (sc0 only: through
+// the L1 into the XCD's L2, which keeps the line instead of writing it
+// through to memory).
 __device__ __forceinline__ void store16_l2(char* base, uint32_t bytes, uint32_t off, u32x4 v) {
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
@@ -943,15 +948,20 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     // every partner slot to carry the same token; the partials are added in
     // slice order, so every slice computes the same total.
     // The slot is written twice, to two regions: into the L2 that the row's
-    // slices share (they are placed on one XCD, above), and through to
-    // memory. Partners poll the first copy through the L2, a shorter round
-    // trip than to memory, and every eighth poll reads the second copy past
-    // the caches, so a placement that puts a partner on another XCD costs
-    // time, never a result. Each row's slots fill one 128-byte line of its
-    // own in each region, so the lines an XCD writes are written by no
-    // other XCD. Against one region at slot b, with cache-bypassing polls:
-    // N = 8, t = 8, d = 8192 chains 3.20-3.30 -> 2.95 us (4 slices), LL
-    // 4.34-4.40 -> 4.09 us (8 slices), FP4 t = 1 3.04-3.19 -> 2.86 us.
+    // slices share (they are placed on one XCD, above; store16_l2), and
+    // through to memory (store16_through). Partners poll with the re-read
+    // of the arrival checks (a volatile buffer load, which the compiler
+    // issues with sc0 sc1; reread16_l2 is the same load): seven polls in
+    // eight read the first copy, which
+    // a partner on the same XCD finds in that XCD's L2, and every eighth
+    // reads the second, so a placement that puts a partner on another XCD
+    // costs time, never a result. Each row's slots fill one 128-byte line of
+    // its own in each region, so the lines an XCD writes are written by no
+    // other XCD. Against one region at slot b, written through, slices on
+    // different XCDs: N = 8, t = 8, d = 8192 chains 3.20-3.30 -> 2.95 us (4
+    // slices), LL 4.34-4.40 -> 4.09 us (8 slices), FP4 t = 1 3.04-3.19 ->
+    // 2.86 us. Polls of the first copy with sc0 alone (not volatile, kept in
+    // the loop by a compiler barrier) were 0.2-0.7 us slower per call.
     __shared__ double xsum;
     if (lane < kWave) {
       const u32x2 tok = dispatch_token();
