@@ -1016,7 +1016,7 @@ def main(argv=None):
                     help="only the timed prefill workload (no decode map, no t=512 figures)")
     ap.add_argument("--all-extras", action="store_true",
                     help="also run every secondary measurement (into --extras-out)")
-    ap.add_argument("--extras-out", default=os.path.join("gpurun_out", "bench_extras.json"),
+    ap.add_argument("--extras-out", default=os.path.join("bench_out", "bench_extras.json"),
                     help="JSON file for the full records of every secondary measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-reps", type=int, default=200,
