@@ -46,7 +46,7 @@ def draw(case: int):
     return n, t, d, layout, split, kw
 
 
-CASES = list(range(48))
+CASES = list(range(160))
 
 
 @pytest.mark.parametrize("case", CASES)
