@@ -1007,6 +1007,19 @@ def bench_record(name, n, t, d, steps, warmup, ms, ms_p50, value, achieved, traf
 
 # ------------------------------------------------------------ main
 
+def build_if_missing() -> None:
+    """Compile the HIP library in-tree when it has not been built (the
+    benchmark runs what is built; it builds only when nothing is)."""
+    pkg = os.path.join(os.path.dirname(os.path.abspath(__file__)), "reduce_residual_rmsnorm_amd")
+    if os.path.exists(os.path.join(pkg, "lib", "libarfuse.so")):
+        return
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("arfuse_build", os.path.join(pkg, "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    log("library not built: building %s" % mod.build())
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -1046,6 +1059,7 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    build_if_missing()
     import reduce_residual_rmsnorm_amd as arf
     import seeded_inputs as si
 

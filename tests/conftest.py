@@ -13,6 +13,9 @@ if HERE not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    # the tests run what is built; they build only when nothing is
+    import __graft_entry__
+    __graft_entry__.build_if_missing()
 
 
 @pytest.fixture(scope="session")
