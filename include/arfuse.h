@@ -93,8 +93,10 @@ typedef enum {
   /* the HIP runtime refused the launch; the returned value also carries the
    * runtime's hipError_t in bits 8 and up (status & 0xFF == 3) */
   ARFUSE_ERR_LAUNCH = 3,
-  /* device side only (arfuse_ll_status.code): some LL word still carried a
-   * flag other than the expected one after max_polls re-reads */
+  /* device side only (arfuse_ll_status.code): something a row waits for
+   * did not arrive within its bounded wait (an LL word still carried
+   * another flag, or a sentinel vector still held the pattern, after
+   * max_polls re-reads; or a split row's partner share never came) */
   ARFUSE_ERR_FLAG_TIMEOUT = 4
 } arfuse_status;
 
@@ -382,10 +384,10 @@ int arfuse_stream_copy(void* dst, const void* src, int64_t bytes, void* stream);
  * uses for that t and d, non-temporal loads, and the fused call's
  * write-through stores where its rows take several rounds of workgroups,
  * else non-temporal stores; every load of a row is issued before the first
- * store. The time of a call is the bandwidth
- * ceiling of the fused call's memory traffic at that shape (Deep Dive §6.1,
- * §6.4: the fused kernel's cost is its HBM transactions). n_in in [1, 9],
- * n_out in [1, 3]; d % 16 == 0, d <= ARFUSE_MAX_D.
+ * store. The time of a call is a reference for the fused call's memory
+ * traffic at that shape: the same bytes without the arithmetic (Deep Dive
+ * §6.1, §6.4: the fused kernel's cost is its HBM transactions). n_in in
+ * [1, 9], n_out in [1, 3]; d % 16 == 0, d <= ARFUSE_MAX_D.
  */
 int arfuse_stream_mix(const void* const* in, int n_in, void* const* out, int n_out, int64_t t,
                       int64_t d, void* stream);
