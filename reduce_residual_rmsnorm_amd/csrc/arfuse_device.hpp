@@ -846,8 +846,8 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
       }
     }
   };
-  // chunk k's share of the sum of squares; without a norm, or in a split
-  // row, its residual_out.
+  // chunk k's share of the sum of squares; without a norm (except in a
+  // streaming row, below), or in a split row, its residual_out.
   // A whole row that normalizes stores residual_out next to y, in the output
   // loop, so the row's two output streams reach HBM together, after its
   // reads, rather than one in the middle of them. Prefill N=8 d=8192: t=4096
@@ -856,7 +856,7 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
   // whose wait the stores then overlap: 160-call chains 0.03-0.12 us faster
   // (FP4 t=64 3.24 -> 3.17 us, N=8 t=8 3.01 -> 2.94, LL N=8 4.08 -> 4.04).
   auto after_sum = [&](int k) {
-    if constexpr (!NORM || SPLIT) store_residual(k);
+    if constexpr ((!NORM && !(STREAM && ALL_AT_ONCE)) || SPLIT) store_residual(k);
     if constexpr (NORM) {
       // h is fp32, so h * h is exact in fp64 and the fused multiply-add
       // rounds exactly as the separate product and sum would
@@ -929,6 +929,15 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
     atomicOr(&a.status->code, (uint32_t)ARFUSE_ERR_FLAG_TIMEOUT);
   }
   if constexpr (!NORM) {
+    // the all-reduce alone in a streaming row: residual_out after a
+    // workgroup barrier, so the row's stores leave together once all of its
+    // reads are in, as a normalizing row's do (t=4096: 111.5-111.7 ->
+    // 110.7-110.9 us, without residual 96.8-97.4 -> 96.3-96.5)
+    if constexpr (STREAM && ALL_AT_ONCE) {
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) store_residual(k);
+    }
     reset_row();
     return;
   }
