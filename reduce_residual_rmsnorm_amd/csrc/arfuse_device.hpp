@@ -751,11 +751,16 @@ __global__ __launch_bounds__(kMaxBlock) void row_kernel(RowArgs a) {
         raw[k][i][0] = load16<true>(at<u32x4>(prow[i], eo[k][0] * 4));
         raw[k][i][1] = load16<true>(at<u32x4>(prow[i], eo[k][1] * 4));
       } else {
-        // the all-reduce alone in a streaming row reads partial 0 with the
-        // default policy: t=4096 107.3-107.6 -> 100.5-100.8 us, without
-        // residual 95.5-95.7 -> 89.2-89.3. (A normalizing row, which
-        // already reads gamma with that policy, lost 7% with it.)
-        if (STREAM && !NORM && i == 0)
+        // partial 0 with the default policy instead of non-temporal, where
+        // measured faster: the all-reduce alone in a streaming row with
+        // N >= 6 (t=4096, N=8: 107.3-107.6 -> 100.5-100.8 us, without
+        // residual 95.5-95.7 -> 89.2-89.3; N=6: 86.4-86.8 -> 80.8-80.9),
+        // and a normalizing one-round row with N = 8 (t=512: 15.80-15.91 ->
+        // 15.63-15.65 us). The other cases lost: the all-reduce at N=4 (62.8-
+        // 63.1 -> 68.5-68.9), normalizing one-round rows at N=6 and 4 (3-7%),
+        // normalizing streaming rows (7%), and two default-policy partials
+        // at t=512 (10%).
+        if (i == 0 && ((STREAM && !NORM && N >= 6) || (KIND == kRowWhole && NORM && N == 8 && !SENT)))
           raw[k][i][0] = load16<false>(at<u32x4>(prow[i], eo[k][0] * 2));
         else
           raw[k][i][0] = load16<true>(at<u32x4>(prow[i], eo[k][0] * 2));
