@@ -223,7 +223,7 @@ typedef struct {
                            the choice for ARFUSE_SPLIT_AUTO) */
   int32_t stream_stores; /* 1: the outputs are written through to memory
                            (calls whose rows take several rounds of
-                           workgroups: t * vpt >= 1024, not LL); 0: they
+                           workgroups: t * vpt >= 1536, not LL); 0: they
                            stay in the caches for the next call (whole
                            rows: default-policy stores, written back at
                            the end of the kernel; split rows: non-temporal

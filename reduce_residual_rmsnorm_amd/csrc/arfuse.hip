@@ -257,10 +257,13 @@ constexpr int64_t kSpreadResetRows = 128;
 
 // Rows times vectors per thread at and above which a call runs the
 // streaming-store instances (kRowStream; see out_store): several rounds of
-// workgroups, prefill. Measured better at t=4096 (VPT 1) and t=1024 (VPT 4),
-// no better at t=512 (VPT 1, one round), worse at decode. LL rows have no
-// streaming instances (their words are decode-sized by design).
-constexpr int64_t kStreamStoreChunks = 1024;
+// workgroups, prefill. N=8 against the whole-row instances: faster at
+// t*VPT = 1536 (t=1536 d=8192: 46.4 against 48.7 us), 2048 (t=2048 d=8192:
+// 60.5 against 66.7; t=1024 d=16384: 62.0 against 69.3) and above; slower
+// at 1024 (t=1024 d=8192: 32.2 against 30.45; t=512 d=16384: 32.9 against
+// 31.9) and below, and at decode. LL rows have no streaming instances
+// (their words are decode-sized by design).
+constexpr int64_t kStreamStoreChunks = 1536;
 
 int row_kind(int64_t t, int lg, int vpt, int layout) {
   if (lg != 0) return kRowSplit;

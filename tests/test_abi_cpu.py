@@ -397,16 +397,19 @@ def test_auto_split_choice_without_norm(shape, split):
 
 
 def test_query_launch_reports_streaming_stores():
-    """Calls whose rows take several rounds of workgroups (t * vpt >= 1024)
-    write their outputs through to memory; decode-sized calls, split rows and
-    LL calls keep non-temporal stores."""
+    """Calls whose rows take three or more rounds of workgroups (t * vpt >=
+    1536) write their outputs through to memory; smaller calls, split rows and
+    LL calls keep the other instances."""
     q = arf.arfuse_query_launch
     assert q(8, 4096, 8192).stream_stores == 1
-    assert q(8, 1024, 8192).stream_stores == 1
-    assert q(8, 1023, 8192).stream_stores == 0
+    assert q(8, 1536, 8192).stream_stores == 1
+    assert q(8, 1535, 8192).stream_stores == 0
+    assert q(8, 1024, 8192).stream_stores == 0
     assert q(8, 512, 8192).stream_stores == 0
-    assert q(2, 256, 32768).stream_stores == 1          # vpt 4
-    assert q(8, 128, 65536).stream_stores == 1          # vpt 8
+    assert q(2, 384, 32768).stream_stores == 1          # vpt 4
+    assert q(2, 256, 32768).stream_stores == 0
+    assert q(8, 192, 65536).stream_stores == 1          # vpt 8
+    assert q(8, 128, 65536).stream_stores == 0
     assert q(8, 4096, 8192, layout=arf.ARFUSE_LAYOUT_LL).stream_stores == 0
     assert q(8, 4096, 8192, layout=arf.ARFUSE_LAYOUT_SENTINEL).stream_stores == 1
     assert q(8, 8, 8192, split=4).stream_stores == 0

@@ -348,7 +348,7 @@ def test_sentinel_triple_buffered_chain_in_graph(split):
         torch.cuda.synchronize()
 
 
-# Calls whose rows take several rounds of workgroups (t * vpt >= 1024) run
+# Calls whose rows take several rounds of workgroups (t * vpt >= 1536) run
 # the instances that write their outputs through to memory (streaming
 # stores); every output kind goes through them here, in the plain and the
 # sentinel layout, and in a wide row (four vectors per thread).
@@ -367,7 +367,7 @@ STREAM_PATTERNS = {
 @pytest.mark.parametrize("pattern", sorted(STREAM_PATTERNS))
 def test_streaming_store_instances(pattern, layout):
     kw = STREAM_PATTERNS[pattern]
-    n, t, d = 3, 1024, 1024
+    n, t, d = 3, 1536, 1024
     epi = ((arf.ARFUSE_EPI_BF16 if kw.get("out", True) and kw.get("gamma", True) else 0)
            | (arf.ARFUSE_EPI_FP4 if kw.get("fp4") else 0)
            | (arf.ARFUSE_EPI_FP8 if kw.get("fp8") is not None else 0))
@@ -393,7 +393,7 @@ def test_streaming_store_instances(pattern, layout):
 
 
 def test_streaming_store_wide_rows():
-    n, t, d = 2, 256, 32768
+    n, t, d = 2, 384, 32768
     info = arf.arfuse_query_launch(n, t, d, arf.ARFUSE_EPI_BF16 | arf.ARFUSE_EPI_FP4)
     assert info.vpt == 4 and info.stream_stores == 1
     ci = si.make_call(n, t, d, seed=120, outlier_frac=0.01)
